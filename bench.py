@@ -1,0 +1,241 @@
+#!/usr/bin/env python3
+"""Throughput of the fused stencil kernels on one MI355X.
+
+One step = one pass of every operation of the library over its full-size
+synthetic workload, on inputs already resident in HBM:
+  conv        x fp32 [128,8,256,256] -> conv 8->64 k3 + tanh + *2 + bias + maxpool 4
+              -> [128,64,63,63]        (74.91 GFLOP: the 252x252 conv outputs the pool reads)
+  maxpool     x fp32 [32,64,512,512] -> k4 s1 p1 d1 -> [32,64,511,511]
+              (4.2866 GB: every input read once + every output written once)
+  convT       x fp32 [128,64,64,64] -> convT 64->128 k4 s2 p1 op1 + softmax + bias + *2
+              + sigmoid -> [128,128,129,129]   (136.37 GFLOP over the valid taps)
+  conv_bf16   the conv workload with bf16 x, w and output (74.91 GFLOP)
+
+`value` is the fused conv+maxpool throughput (GFLOP/s, fp32) -- the first
+figure of the headline metric; the max-pool's GB/s (the second figure) and the
+other two operations are reported in `ops` of the same line, each with its
+roofline fraction.  Per-kernel times come from HIP events recorded on the
+stream the kernels run on (torch's current stream), averaged over the timed
+steps.  Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP32 = 157.3e12      # MI355X dense fp32 (vector or matrix), FLOP/s
+PEAK_BF16 = 2.5e15        # MI355X dense bf16 matrix, FLOP/s
+PEAK_HBM = 8.0e12         # MI355X HBM3E, B/s
+
+CONV_FLOP = 2 * 72 * 128 * 64 * 252 * 252
+CONV_FLOP_PAGE = 2 * 72 * 128 * 64 * 254 * 254     # the page's count over all 254x254 outputs
+POOL_BYTES = 32 * 64 * 512 * 512 * 4 + 32 * 64 * 511 * 511 * 4
+CONVT_FLOP = 2 * 128 * 64 * 128 * 255 * 255
+CONVT_BYTES = 128 * 64 * 64 * 64 * 4 + 128 * 128 * 129 * 129 * 4 + 64 * 128 * 16 * 4
+
+# HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE (profiles/), scaled
+# by the copy-kernel calibration factor; None until measured for the current kernels.
+TRAFFIC = {"conv": None, "maxpool": None, "convT": None, "conv_bf16": None}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle timing (profiling runs)")
+    ap.add_argument("--ops", default="conv,maxpool,convT,conv_bf16")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
+              "the operations shard over the batch with no communication, so the one-GPU "
+              "figure is the per-GPU figure", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import inputgen
+    import pool_stencil_amd as ps
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ops = [o for o in args.ops.split(",") if o]
+    t0 = time.time()
+
+    def put(a, dtype=None):
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        if dtype is not None:
+            t = t.view(dtype)
+        return t.to(dev)
+
+    runs = {}
+    if "conv" in ops:
+        c = inputgen.workload("conv")
+        xd, wd, cb, b2 = put(c["x"]), put(c["w"]), put(c["conv_bias"]), put(c["bias2"])
+        out = torch.empty((128, 64, 63, 63), dtype=torch.float32, device=dev)
+        runs["conv"] = lambda xd=xd, wd=wd, cb=cb, b2=b2, out=out: ps.conv_tanh_scale_bias_maxpool(
+            xd, wd, cb, b2, 2.0, 4, out=out)
+        del c
+    if "maxpool" in ops:
+        c = inputgen.workload("maxpool")
+        xp = put(c["x"])
+        outp = torch.empty((32, 64, 511, 511), dtype=torch.float32, device=dev)
+        runs["maxpool"] = lambda xp=xp, outp=outp: ps.maxpool2d(xp, 4, 1, 1, 1, out=outp)
+        del c
+    if "convT" in ops:
+        c = inputgen.workload("convT")
+        xt, wt, cbt, b2t = put(c["x"]), put(c["w"]), put(c["convT_bias"]), put(c["bias2"])
+        outt = torch.empty((128, 128, 129, 129), dtype=torch.float32, device=dev)
+        runs["convT"] = lambda xt=xt, wt=wt, cbt=cbt, b2t=b2t, outt=outt: (
+            ps.convT_softmax_bias_scale_sigmoid(xt, wt, cbt, b2t, 2.0, 2, 1, 1, 1, out=outt))
+        del c
+    if "conv_bf16" in ops:
+        c = inputgen.workload("conv_bf16")
+        xb = put(c["x_bits"].view(np.int16)).view(torch.bfloat16)
+        wb = put(c["w_bits"].view(np.int16)).view(torch.bfloat16)
+        cbb, b2b = put(c["conv_bias"]), put(c["bias2"])
+        outb = torch.empty((128, 64, 63, 63), dtype=torch.bfloat16, device=dev)
+        runs["conv_bf16"] = lambda xb=xb, wb=wb, cbb=cbb, b2b=b2b, outb=outb: (
+            ps.conv_tanh_scale_bias_maxpool(xb, wb, cbb, b2b, 2.0, 4, out=outb))
+        del c
+    torch.cuda.synchronize()
+    print(f"[bench] inputs ready in {time.time() - t0:.1f}s; ops {list(runs)}",
+          file=sys.stderr, flush=True)
+
+    for i in range(args.warmup):
+        for name, fn in runs.items():
+            fn()
+    torch.cuda.synchronize()
+    print("[bench] warmup done", file=sys.stderr, flush=True)
+
+    ev = {name: [] for name in runs}
+    step_start = torch.cuda.Event(enable_timing=True)
+    step_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    step_start.record()
+    for i in range(args.steps):
+        for name, fn in runs.items():
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            ev[name].append((a, b))
+    step_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = step_start.elapsed_time(step_end)
+    ms = {name: [a.elapsed_time(b) for a, b in pairs] for name, pairs in ev.items()}
+    print(f"[bench] timed {args.steps} steps in {wall:.2f}s", file=sys.stderr, flush=True)
+
+    def stats(name):
+        v = np.array(ms[name])
+        return float(v.mean()), float(np.median(v)), float(v.min())
+
+    out_ops = {}
+    if "conv" in runs:
+        mean, med, mn = stats("conv")
+        ach = CONV_FLOP / (mean * 1e-3)
+        out_ops["conv"] = {
+            "value": ach / 1e9, "unit": "GFLOP/s", "ms_mean": mean, "ms_median": med, "ms_min": mn,
+            "gflop_per_launch": CONV_FLOP / 1e9,
+            "value_page_count": CONV_FLOP_PAGE / (mean * 1e-3) / 1e9,
+            "roofline": {"bound": "mfma", "achieved": ach / 1e12, "peak": PEAK_FP32 / 1e12,
+                         "unit": "TFLOP/s", "frac": ach / PEAK_FP32, "traffic": TRAFFIC["conv"]}}
+    if "maxpool" in runs:
+        mean, med, mn = stats("maxpool")
+        ach = POOL_BYTES / (mean * 1e-3)
+        out_ops["maxpool"] = {
+            "value": ach / 1e9, "unit": "GB/s", "ms_mean": mean, "ms_median": med, "ms_min": mn,
+            "gbytes_per_launch": POOL_BYTES / 1e9,
+            "roofline": {"bound": "hbm", "achieved": ach / 1e9, "peak": PEAK_HBM / 1e9,
+                         "unit": "GB/s", "frac": ach / PEAK_HBM, "traffic": TRAFFIC["maxpool"]}}
+    if "convT" in runs:
+        mean, med, mn = stats("convT")
+        ach = CONVT_FLOP / (mean * 1e-3)
+        out_ops["convT"] = {
+            "value": ach / 1e9, "unit": "GFLOP/s", "ms_mean": mean, "ms_median": med, "ms_min": mn,
+            "gflop_per_launch": CONVT_FLOP / 1e9,
+            "hbm_GBps": CONVT_BYTES / (mean * 1e-3) / 1e9,
+            "roofline": {"bound": "mfma", "achieved": ach / 1e12, "peak": PEAK_FP32 / 1e12,
+                         "unit": "TFLOP/s", "frac": ach / PEAK_FP32, "traffic": TRAFFIC["convT"]}}
+    if "conv_bf16" in runs:
+        mean, med, mn = stats("conv_bf16")
+        ach = CONV_FLOP / (mean * 1e-3)
+        out_ops["conv_bf16"] = {
+            "value": ach / 1e9, "unit": "GFLOP/s", "ms_mean": mean, "ms_median": med, "ms_min": mn,
+            "gflop_per_launch": CONV_FLOP / 1e9,
+            "roofline": {"bound": "mfma", "achieved": ach / 1e12, "peak": PEAK_BF16 / 1e12,
+                         "unit": "TFLOP/s", "frac": ach / PEAK_BF16, "traffic": TRAFFIC["conv_bf16"],
+                         "frac_of_fp32_peak": ach / PEAK_FP32}}
+
+    head = "conv" if "conv" in out_ops else next(iter(out_ops))
+    cpu = None
+    if not args.no_cpu_baseline and head == "conv":
+        cpu = cpu_baseline()
+
+    line = {
+        "metric": "fused conv+maxpool GFLOP/s & maxpool GB/s, % of MI355X roofline, 1 GPU",
+        "value": out_ops[head]["value"],
+        "unit": out_ops[head]["unit"],
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": total_ms / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "conv2d 8->64 k3 + tanh + *2 + bias + maxpool4, x fp32 [128,8,256,256] "
+                        "-> [128,64,63,63]",
+            "step": list(runs),
+            "maxpool_workload": "maxpool2d k4 s1 p1 d1, x fp32 [32,64,512,512] -> [32,64,511,511]",
+            "convT_workload": "convT 64->128 k4 s2 p1 op1 + softmax(c) + bias + *2 + sigmoid, "
+                              "x fp32 [128,64,64,64] -> [128,128,129,129]",
+            "conv_bf16_workload": "conv workload with bf16 x/w/out, fp32 accumulate",
+        },
+        "roofline": out_ops[head]["roofline"],
+        "cpu_baseline": cpu,
+        "maxpool_GBps": out_ops.get("maxpool", {}).get("value"),
+        "ops": out_ops,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline():
+    """The oracle (plain C, fp64, OpenMP) on a bounded slice of the conv workload."""
+    import oracle
+    import inputgen
+    c = inputgen.workload("conv")
+    n_img = int(os.environ.get("PS_CPU_IMAGES", "4"))
+    c1 = dict(c)
+    c1["x"] = c["x"][:n_img]
+    c1["N"] = n_img
+    t = time.perf_counter()
+    oracle.conv_tanh_scale_bias_maxpool(c1)
+    dt = time.perf_counter() - t
+    flop = CONV_FLOP / 128 * n_img
+    return {"value": flop / dt / 1e9, "unit": "GFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "seconds": dt,
+            "sample": f"first {n_img} of 128 images of the conv workload (full fused op in "
+                      f"written order, double precision); GFLOP counted as for the GPU"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,223 @@
+// MaxPool2d kernels for gfx950.
+//
+// Definition (POPCORNBENCH page Kimi-K2.6 l1_p42, problem statement and the
+// passage on PyTorch's implicit negative-infinity padding):
+//   y[n,c,oh,ow] = max_{kh,kw<k} x[n,c, oh*s - p + kh*d, ow*s - p + kw*d],
+//   positions outside the image count as -inf, floor mode.
+//
+// Two kernels:
+//   maxpool_s1_rows  stride 1, dilation 1, window k <= 8, pad < k.  The case
+//                    that is pure HBM streaming (every input is read about once,
+//                    every output written once).  One wavefront owns a band of
+//                    output rows of one (n,c) plane and a strip of 64*V output
+//                    columns.  It walks the input rows of its band top to bottom:
+//                      - each input row is loaded once, as V+1 fully coalesced
+//                        256-byte wave loads (lane l holds column 64j + l);
+//                      - the horizontal k-max is formed in registers by
+//                        rotating the row across lanes (ds_bpermute), using
+//                        doubling windows (1 -> 2 -> 4 -> 8) so a k=4 window costs
+//                        two rotations per chunk instead of three;
+//                      - the last k horizontal maxima are kept in a register
+//                        ring, and each output row is the max down that ring
+//                        (the separable max of the l1_p42 page, done in
+//                        registers rather than through a shared-memory tile);
+//                      - each output row is written as V coalesced wave stores.
+//                    The band's k-1 halo rows are the only re-reads; four
+//                    consecutive bands of a plane share a workgroup, so the
+//                    halo is served by L1/L2.
+//   maxpool_direct   any k, stride, pad, dilation: one thread per output,
+//                    window read through the cache hierarchy.
+#include "ps_internal.h"
+
+#include <math.h>
+
+namespace ps {
+namespace {
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float rot_lanes(float v, int src_lane_x4) {
+    return __int_as_float(__builtin_amdgcn_ds_bpermute(src_lane_x4, __float_as_int(v)));
+}
+
+__device__ __forceinline__ float fmax_ordered(float a, float b) { return b > a ? b : a; }
+
+// hw[j] <- max over the window [64j + lane, 64j + lane + span) of the row held in
+// chunks v[0..V] (chunk j lane l = element 64j + l), given that v already holds the
+// window-`have` maxima.  Shifts by `have` lanes with carry from the next chunk.
+template <int V>
+__device__ __forceinline__ void widen(float (&v)[V + 1], int lane, int shift) {
+    const int src = ((lane + shift) & (kWave - 1)) << 2;
+    const bool carry = lane + shift >= kWave;
+    float rot[V + 1];
+#pragma unroll
+    for (int j = 0; j <= V; ++j) rot[j] = rot_lanes(v[j], src);
+#pragma unroll
+    for (int j = 0; j < V; ++j) v[j] = fmax_ordered(v[j], carry ? rot[j + 1] : rot[j]);
+    // chunk V only feeds the lanes of chunk V-1 that carry into it; its own
+    // widened value is never used as an output.
+    v[V] = fmax_ordered(v[V], rot[V]);
+}
+
+template <int K, int V>
+__global__ __launch_bounds__(256) void maxpool_s1_rows(
+    const float *__restrict__ x, float *__restrict__ y, int H, int W, int OH, int OW, int pad,
+    int band_rows, int nbands, int nstrips, uint64_t ntasks) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x >> 6;
+    const uint32_t blk = xcd_remap(blockIdx.x, gridDim.x);
+    const uint64_t task = (uint64_t)blk * (blockDim.x >> 6) + wave;
+    if (task >= ntasks) return;
+    const int band = (int)(task % (uint64_t)nbands);
+    const uint64_t t2 = task / (uint64_t)nbands;
+    const int strip = (int)(t2 % (uint64_t)nstrips);
+    const uint64_t plane = t2 / (uint64_t)nstrips;
+
+    const float *xp = x + plane * (uint64_t)H * W;
+    float *yp = y + plane * (uint64_t)OH * OW;
+    const int c0 = strip * (kWave * V);  // first output column of the strip
+    const int ic0 = c0 - pad;            // input column under lane 0 of chunk 0
+    const int oh0 = band * band_rows;
+    const int oh1 = min(OH, oh0 + band_rows);
+    const int ih_first = oh0 - pad;
+    const int ih_last = oh1 - 1 - pad + K - 1;
+
+    // Column validity is fixed for the whole band.
+    bool colok[V + 1];
+#pragma unroll
+    for (int j = 0; j <= V; ++j) {
+        const int c = ic0 + kWave * j + lane;
+        colok[j] = (c >= 0) && (c < W);
+    }
+
+    auto load_row = [&](int ih, float (&v)[V + 1]) {
+        const bool rowok = (ih >= 0) && (ih < H);
+        const float *rp = xp + (int64_t)ih * W + ic0 + lane;
+#pragma unroll
+        for (int j = 0; j <= V; ++j)
+            v[j] = (rowok && colok[j]) ? rp[kWave * j] : -INFINITY;
+    };
+
+    float ring[K][V];
+    float nxt[V + 1];
+    load_row(ih_first, nxt);
+    int ih = ih_first;
+    for (int r = 0; ih <= ih_last; ++r, ++ih) {
+        float v[V + 1];
+#pragma unroll
+        for (int j = 0; j <= V; ++j) v[j] = nxt[j];
+        if (ih < ih_last) load_row(ih + 1, nxt);  // one row of prefetch in flight
+
+        // horizontal window-K max by doubling: window 1 -> 2 -> 4 (-> 8)
+        constexpr int P = K >= 8 ? 8 : K >= 4 ? 4 : K >= 2 ? 2 : 1;  // largest power of 2 <= K
+        if constexpr (P >= 2) widen<V>(v, lane, 1);
+        if constexpr (P >= 4) widen<V>(v, lane, 2);
+        if constexpr (P >= 8) widen<V>(v, lane, 4);
+        if constexpr (K != P) {
+            // window K = window P at c  combined with window P at c + (K - P)
+            float w2[V + 1];
+#pragma unroll
+            for (int j = 0; j <= V; ++j) w2[j] = v[j];
+            const int sh = K - P;
+            const int src = ((lane + sh) & (kWave - 1)) << 2;
+            const bool carry = lane + sh >= kWave;
+            float rot[V + 1];
+#pragma unroll
+            for (int j = 0; j <= V; ++j) rot[j] = rot_lanes(w2[j], src);
+#pragma unroll
+            for (int j = 0; j < V; ++j) v[j] = fmax_ordered(v[j], carry ? rot[j + 1] : rot[j]);
+        }
+
+        // shift the vertical ring and append this row's horizontal maxima
+#pragma unroll
+        for (int i = 0; i < K - 1; ++i)
+#pragma unroll
+            for (int j = 0; j < V; ++j) ring[i][j] = ring[i + 1][j];
+#pragma unroll
+        for (int j = 0; j < V; ++j) ring[K - 1][j] = v[j];
+
+        if (r >= K - 1) {
+            const int oh = ih - (K - 1) + pad;
+            float *orow = yp + (int64_t)oh * OW + c0 + lane;
+#pragma unroll
+            for (int j = 0; j < V; ++j) {
+                float m = ring[0][j];
+#pragma unroll
+                for (int i = 1; i < K; ++i) m = fmax_ordered(m, ring[i][j]);
+                if (c0 + kWave * j + lane < OW) orow[kWave * j] = m;
+            }
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void maxpool_direct(const float *__restrict__ x,
+                                                      float *__restrict__ y, int H, int W,
+                                                      int OH, int OW, int k, int s, int p, int d,
+                                                      uint64_t total) {
+    const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= total) return;
+    const int ow = (int)(i % (uint64_t)OW);
+    const int oh = (int)((i / (uint64_t)OW) % (uint64_t)OH);
+    const uint64_t plane = i / ((uint64_t)OW * OH);
+    const float *xp = x + plane * (uint64_t)H * W;
+    float m = -INFINITY;
+    for (int kh = 0; kh < k; ++kh) {
+        const int ih = oh * s - p + kh * d;
+        if (ih < 0 || ih >= H) continue;
+        for (int kw = 0; kw < k; ++kw) {
+            const int iw = ow * s - p + kw * d;
+            if (iw < 0 || iw >= W) continue;
+            m = fmax_ordered(m, xp[(int64_t)ih * W + iw]);
+        }
+    }
+    y[i] = m;
+}
+
+template <int K, int V>
+int launch_rows(const float *x, float *y, int N, int C, int H, int W, int OH, int OW, int p,
+                hipStream_t stream) {
+    const int band_rows = 32;
+    const int nbands = (OH + band_rows - 1) / band_rows;
+    const int nstrips = (OW + kWave * V - 1) / (kWave * V);
+    const uint64_t ntasks = (uint64_t)N * C * nstrips * nbands;
+    const uint64_t nblocks = (ntasks + 3) / 4;
+    if (nblocks > 0x7fffffffull) return PS_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL((maxpool_s1_rows<K, V>), dim3((unsigned)nblocks), dim3(256), 0, stream,
+                       x, y, H, W, OH, OW, p, band_rows, nbands, nstrips, ntasks);
+    return hipGetLastError() == hipSuccess ? PS_OK : PS_ERR_HIP;
+}
+
+template <int K>
+int launch_rows_k(const float *x, float *y, int N, int C, int H, int W, int OH, int OW, int p,
+                  hipStream_t stream) {
+    // strip width 64*V: one strip covers rows up to 512 outputs wide
+    if (OW > 256) return launch_rows<K, 8>(x, y, N, C, H, W, OH, OW, p, stream);
+    if (OW > 128) return launch_rows<K, 4>(x, y, N, C, H, W, OH, OW, p, stream);
+    if (OW > 64) return launch_rows<K, 2>(x, y, N, C, H, W, OH, OW, p, stream);
+    return launch_rows<K, 1>(x, y, N, C, H, W, OH, OW, p, stream);
+}
+
+}  // namespace
+
+int launch_maxpool2d(const float *x, float *y, int N, int C, int H, int W, int OH, int OW,
+                     int k, int s, int p, int d, hipStream_t stream) {
+    if (s == 1 && d == 1 && p < k && k >= 2 && k <= 8) {
+        switch (k) {
+            case 2: return launch_rows_k<2>(x, y, N, C, H, W, OH, OW, p, stream);
+            case 3: return launch_rows_k<3>(x, y, N, C, H, W, OH, OW, p, stream);
+            case 4: return launch_rows_k<4>(x, y, N, C, H, W, OH, OW, p, stream);
+            case 5: return launch_rows_k<5>(x, y, N, C, H, W, OH, OW, p, stream);
+            case 6: return launch_rows_k<6>(x, y, N, C, H, W, OH, OW, p, stream);
+            case 7: return launch_rows_k<7>(x, y, N, C, H, W, OH, OW, p, stream);
+            case 8: return launch_rows_k<8>(x, y, N, C, H, W, OH, OW, p, stream);
+        }
+    }
+    const uint64_t total = (uint64_t)N * C * OH * OW;
+    const uint64_t nblocks = (total + 255) / 256;
+    if (nblocks > 0x7fffffffull) return PS_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL(maxpool_direct, dim3((unsigned)nblocks), dim3(256), 0, stream, x, y, H, W,
+                       OH, OW, k, s, p, d, total);
+    return hipGetLastError() == hipSuccess ? PS_OK : PS_ERR_HIP;
+}
+
+}  // namespace ps

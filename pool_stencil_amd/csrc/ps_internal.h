@@ -1,0 +1,41 @@
+// Internal declarations shared by the HIP translation units of libpool_stencil.
+// Not part of the public C ABI (that is include/pool_stencil.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pool_stencil.h"
+
+namespace ps {
+
+// Launchers.  Arguments have already been validated by the entry points in
+// api.hip; each returns PS_OK or PS_ERR_HIP.
+int launch_maxpool2d(const float *x, float *y, int N, int C, int H, int W, int OH, int OW,
+                     int k, int s, int p, int d, hipStream_t stream);
+
+int launch_conv_pool(const void *x, const void *w, const float *conv_bias, const float *bias2,
+                     void *y, int dtype, int N, int Cin, int H, int W, int Cout, int conv_pad,
+                     int OH, int OW, float scale, int pool_k, int PH, int PW,
+                     hipStream_t stream);
+
+int launch_convT_softmax(const float *x, const float *w, const float *convT_bias,
+                         const float *bias2, float *y, int N, int Cin, int H, int W, int Cout,
+                         int OH, int OW, float scale, hipStream_t stream);
+
+// Blocks of one launch are handed to the 8 XCDs of an MI355X round-robin
+// (block b runs on XCD b % 8).  This remaps the hardware block index so that
+// consecutive LOGICAL blocks (which share halo rows and weights) run on the
+// same XCD and therefore share its L2.  A bijection on [0, nblocks).
+__device__ __forceinline__ uint32_t xcd_remap(uint32_t b, uint32_t nblocks) {
+    constexpr uint32_t kXcd = 8;
+    const uint32_t per = nblocks / kXcd;          // full rounds
+    const uint32_t tail = nblocks - per * kXcd;   // blocks of the last partial round
+    const uint32_t xcd = b % kXcd;
+    const uint32_t pos = b / kXcd;
+    // XCD x owns per (+1 if x < tail) logical blocks, in order.
+    const uint32_t start = xcd * per + (xcd < tail ? xcd : tail);
+    return start + pos;
+}
+
+}  // namespace ps

@@ -1,0 +1,142 @@
+"""Host-side checks of the C ABI: the library loads, exports every symbol the
+header declares, and validates arguments before touching a device.  No test
+here launches a kernel (fake device pointers are only passed where validation
+must reject the call first)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def ps():
+    lib_path = os.path.join(ROOT, "pool_stencil_amd", "libpool_stencil.so")
+    if not os.path.exists(lib_path):
+        from pool_stencil_amd import build as b
+        b.build()
+    import pool_stencil_amd
+    return pool_stencil_amd
+
+
+def _header_symbols():
+    text = open(os.path.join(ROOT, "include", "pool_stencil.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ps_[A-Za-z0-9_]+)\s*\(", text)))
+
+
+def test_header_symbols_are_exported(ps):
+    syms = _header_symbols()
+    assert len(syms) >= 8
+    assert set(syms) == set(ps.EXPORTS)
+    lib = ps.lib()
+    for s in syms:
+        assert hasattr(lib, s), s
+
+
+def test_status_strings(ps):
+    for st in range(7):
+        s = ps.status_string(st)
+        assert isinstance(s, str) and s
+    assert ps.status_string(99) == "unknown status"
+    assert ps.version() >= 100
+
+
+@pytest.mark.parametrize("n,k,s,p,d", [(256, 3, 1, 0, 1), (254, 4, 4, 0, 1), (512, 4, 1, 1, 1),
+                                       (129, 4, 2, 1, 1), (32, 3, 1, 0, 1), (30, 4, 4, 0, 1),
+                                       (17, 5, 2, 2, 2), (7, 3, 3, 1, 1)])
+def test_window_extent_matches_oracle(ps, n, k, s, p, d):
+    assert ps.conv2d_out_dim(n, k, s, p, d) == oracle.window_out_dim(n, k, s, p, d)
+    assert ps.pool2d_out_dim(n, k, s, p, d) == oracle.window_out_dim(n, k, s, p, d)
+
+
+def test_pool_default_stride(ps):
+    assert ps.pool2d_out_dim(254, 4) == 63
+
+
+@pytest.mark.parametrize("n,k,s,p,op,d", [(64, 4, 2, 1, 1, 1), (64, 4, 2, 1, 0, 1),
+                                          (5, 3, 3, 0, 2, 1), (4, 3, 2, 2, 1, 2)])
+def test_transposed_extent_matches_oracle(ps, n, k, s, p, op, d):
+    assert ps.convT2d_out_dim(n, k, s, p, op, d) == oracle.convT_out_dim(n, k, s, p, op, d)
+
+
+def test_shape_query_errors(ps):
+    lib = ps.lib()
+    out = ctypes.c_int(-7)
+    assert lib.ps_conv2d_out_dim(10, 3, 1, 0, 1, None) == ps.PS_ERR_NULL
+    assert lib.ps_conv2d_out_dim(10, 0, 1, 0, 1, ctypes.byref(out)) == ps.PS_ERR_PARAM
+    assert lib.ps_conv2d_out_dim(10, 3, 0, 0, 1, ctypes.byref(out)) == ps.PS_ERR_PARAM
+    assert lib.ps_conv2d_out_dim(10, 3, 1, -1, 1, ctypes.byref(out)) == ps.PS_ERR_PARAM
+    assert lib.ps_conv2d_out_dim(2, 3, 1, 0, 1, ctypes.byref(out)) == ps.PS_ERR_SHAPE
+    assert lib.ps_conv2d_out_dim(0, 1, 1, 0, 1, ctypes.byref(out)) == ps.PS_ERR_SHAPE
+    assert out.value == -7  # untouched on error
+    # output_padding must be < max(stride, dilation)
+    assert lib.ps_convT2d_out_dim(64, 4, 2, 1, 2, 1, ctypes.byref(out)) == ps.PS_ERR_PARAM
+    assert lib.ps_convT2d_out_dim(64, 4, 2, 1, 1, 1, ctypes.byref(out)) == ps.PS_OK
+    assert out.value == 129
+
+
+FAKE = ctypes.c_void_p(1 << 20)      # aligned, never dereferenced: validation rejects first
+MISALIGNED = ctypes.c_void_p((1 << 20) + 4)
+
+
+def _conv(lib, x=FAKE, w=FAKE, cb=None, b2=FAKE, y=FAKE, dtype=0, N=2, Cin=8, H=32, W=32,
+          Cout=16, kH=3, kW=3, cs=1, cp=0, cd=1, scale=2.0, pk=4, pst=0, pp=0, pd=1):
+    return lib.ps_conv_tanh_scale_bias_maxpool(x, w, cb, b2, y, dtype, N, Cin, H, W, Cout, kH, kW,
+                                               cs, cp, cd, scale, pk, pst, pp, pd, None)
+
+
+def test_conv_pool_validation(ps):
+    lib = ps.lib()
+    assert _conv(lib, x=None) == ps.PS_ERR_NULL
+    assert _conv(lib, b2=None) == ps.PS_ERR_NULL
+    assert _conv(lib, dtype=7) == ps.PS_ERR_PARAM
+    assert _conv(lib, N=0) == ps.PS_ERR_SHAPE
+    assert _conv(lib, H=2) == ps.PS_ERR_SHAPE            # conv window does not fit
+    assert _conv(lib, H=5) == ps.PS_ERR_SHAPE            # conv 3 rows < pool 4
+    assert _conv(lib, cp=-1) == ps.PS_ERR_PARAM
+    assert _conv(lib, kH=5, kW=5) == ps.PS_ERR_UNSUPPORTED
+    assert _conv(lib, cs=2) == ps.PS_ERR_UNSUPPORTED
+    assert _conv(lib, Cin=9) == ps.PS_ERR_UNSUPPORTED
+    assert _conv(lib, pst=2) == ps.PS_ERR_UNSUPPORTED     # overlapping pool windows
+    assert _conv(lib, pk=9) == ps.PS_ERR_UNSUPPORTED
+    assert _conv(lib, x=MISALIGNED) == ps.PS_ERR_ALIGN
+    assert _conv(lib, y=MISALIGNED) == ps.PS_ERR_ALIGN
+
+
+def _pool(lib, x=FAKE, y=FAKE, N=1, C=1, H=8, W=8, k=4, s=1, p=1, d=1):
+    return lib.ps_maxpool2d(x, y, N, C, H, W, k, s, p, d, None)
+
+
+def test_maxpool_validation(ps):
+    lib = ps.lib()
+    assert _pool(lib, x=None) == ps.PS_ERR_NULL
+    assert _pool(lib, H=0) == ps.PS_ERR_SHAPE
+    assert _pool(lib, k=0) == ps.PS_ERR_PARAM
+    assert _pool(lib, p=-1) == ps.PS_ERR_PARAM
+    assert _pool(lib, H=2, p=0) == ps.PS_ERR_SHAPE
+    assert _pool(lib, k=17, H=40, W=40) == ps.PS_ERR_UNSUPPORTED
+    assert _pool(lib, y=MISALIGNED) == ps.PS_ERR_ALIGN
+    assert _pool(lib, N=1 << 20, C=1 << 20) == ps.PS_ERR_SHAPE   # > 2^40 elements
+
+
+def _convT(lib, x=FAKE, w=FAKE, cb=None, b2=FAKE, y=FAKE, N=1, Cin=64, H=8, W=8, Cout=128, k=4,
+           s=2, p=1, op=1, d=1, scale=2.0):
+    return lib.ps_convT_softmax_bias_scale_sigmoid(x, w, cb, b2, y, N, Cin, H, W, Cout, k, s, p,
+                                                   op, d, scale, None)
+
+
+def test_convT_validation(ps):
+    lib = ps.lib()
+    assert _convT(lib, w=None) == ps.PS_ERR_NULL
+    assert _convT(lib, Cout=0) == ps.PS_ERR_SHAPE
+    assert _convT(lib, op=2) == ps.PS_ERR_PARAM
+    assert _convT(lib, k=3) == ps.PS_ERR_UNSUPPORTED
+    assert _convT(lib, s=3) == ps.PS_ERR_UNSUPPORTED
+    assert _convT(lib, Cout=24) == ps.PS_ERR_UNSUPPORTED
+    assert _convT(lib, Cout=144) == ps.PS_ERR_UNSUPPORTED
+    assert _convT(lib, x=MISALIGNED) == ps.PS_ERR_ALIGN

@@ -1,0 +1,254 @@
+"""Parity of the HIP kernels (through the C ABI) against the CPU oracle.
+
+Every case prints its name, shape and seed before its first GPU call.  Sizes:
+small cases the oracle finishes in well under a second, spanning several
+tiles plus ragged tails, and the full workloads (sampled outputs, or the full
+output for the max-pool) in the same launch configuration the benchmark times.
+
+Bars: max-pool bit-exact (a -0/+0 tie counts as equal); fp32 conv paths
+abs 1e-4; bf16 conv path abs 2e-2; every output element written (NaN canary).
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import inputgen
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+F32_TOL = 1e-4
+BF16_TOL = 2e-2
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import pool_stencil_amd  # noqa: F401  (fails loudly if the library is missing)
+    return torch.device("cuda:0")
+
+
+def _say(*a):
+    print("[case]", *a, file=sys.stderr, flush=True)
+
+
+def _dev(a, dev, dtype=None):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.to(dev)
+
+
+def _canary(shape, dev, dtype):
+    import torch
+    return torch.full(shape, float("nan"), dtype=dtype, device=dev)
+
+
+# ----------------------------------------------------------------- maxpool ---
+POOL_CASES = [
+    # (N, C, H, W, k, s, p, d)
+    (2, 3, 37, 45, 4, 1, 1, 1),     # stride-1 row kernel, ragged
+    (1, 2, 70, 512, 4, 1, 1, 1),    # full-width strip, 3 bands
+    (1, 2, 9, 700, 4, 1, 1, 1),     # two strips
+    (2, 2, 33, 130, 3, 1, 1, 1),
+    (1, 3, 20, 64, 2, 1, 0, 1),
+    (1, 1, 40, 300, 5, 1, 2, 1),
+    (1, 1, 40, 200, 7, 1, 3, 1),
+    (1, 1, 19, 90, 8, 1, 0, 1),
+    (1, 1, 5, 5, 4, 1, 3, 1),       # windows at the border only touch padding partly
+    (2, 2, 31, 29, 2, 2, 0, 1),     # direct kernel from here on
+    (1, 2, 25, 27, 3, 2, 1, 1),
+    (1, 1, 17, 21, 3, 1, 1, 2),
+    (1, 1, 1, 1, 2, 1, 1, 2),       # all-padding window -> -inf
+    (1, 2, 12, 14, 4, 4, 0, 1),
+]
+
+
+@pytest.mark.parametrize("case", POOL_CASES)
+def test_maxpool_small(dev, case):
+    import pool_stencil_amd as ps
+    N, C, H, W, k, s, p, d = case
+    _say("maxpool", case, "seed 101")
+    x = inputgen.randn(101, (N, C, H, W))
+    ref = oracle.maxpool2d(x, k, s, p, d)
+    xd = _dev(x, dev)
+    import torch
+    out = _canary(ref.shape, dev, torch.float32)
+    ps.maxpool2d(xd, k, s, p, d, out=out)
+    got = out.cpu().numpy()
+    assert not np.isnan(got).any()
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_maxpool_full_workload(dev):
+    """The full 32x64x512x512 k4 s1 p1 d1 pool, every output compared bit for bit."""
+    import pool_stencil_amd as ps
+    import torch
+    c = inputgen.workload("maxpool")
+    _say("maxpool workload", c["x"].shape)
+    ref = oracle.maxpool2d(c["x"], c["k"], c["stride"], c["pad"], c["dil"])
+    xd = _dev(c["x"], dev)
+    out = _canary(ref.shape, dev, torch.float32)
+    ps.maxpool2d(xd, c["k"], c["stride"], c["pad"], c["dil"], out=out)
+    got = out.cpu().numpy()
+    del xd, out
+    assert got.shape == (32, 64, 511, 511)
+    assert not np.isnan(got).any()
+    np.testing.assert_array_equal(got, ref)
+
+
+# ------------------------------------------------------- fused conv + pool ---
+def _run_conv(c, dev):
+    import pool_stencil_amd as ps
+    import torch
+    if c["dtype"] == "bf16":
+        xd = _dev(c["x_bits"].view(np.int16), dev).view(torch.bfloat16)
+        wd = _dev(c["w_bits"].view(np.int16), dev).view(torch.bfloat16)
+        odt = torch.bfloat16
+    else:
+        xd, wd, odt = _dev(c["x"], dev), _dev(c["w"], dev), torch.float32
+    cb = None if c["conv_bias"] is None else _dev(c["conv_bias"], dev)
+    b2 = _dev(c["bias2"], dev)
+    shape = oracle.conv_pool_out_shape(c)
+    out = _canary(shape, dev, odt)
+    ps.conv_tanh_scale_bias_maxpool(xd, wd, cb, b2, c["scale"], c["pool_k"], c["pool_stride"],
+                                    c["conv_stride"], c["conv_pad"], c["conv_dil"],
+                                    c["pool_pad"], c["pool_dil"], out=out)
+    return out.float().cpu().numpy()
+
+
+CONV_CASES = [
+    dict(N=2, Cin=8, H=32, W=32, Cout=16),                  # the tiny workload's shape
+    dict(N=1, Cin=8, H=70, W=258, Cout=64),                 # 64-wide tiles, ragged tail
+    dict(N=2, Cin=3, H=45, W=71, Cout=20),                  # Cin < 4, Cout ragged
+    dict(N=1, Cin=5, H=30, W=40, Cout=130),                 # three 64-channel tiles
+    dict(N=1, Cin=8, H=21, W=300, Cout=64, conv_pad=1),
+    dict(N=1, Cin=8, H=19, W=33, Cout=32, conv_pad=2),
+    dict(N=1, Cin=8, H=40, W=90, Cout=16, pool_k=2, pool_stride=2),
+    dict(N=1, Cin=4, H=40, W=90, Cout=16, pool_k=3, pool_stride=3),
+    dict(N=1, Cin=8, H=50, W=77, Cout=24, pool_k=5, pool_stride=5),
+    dict(N=1, Cin=8, H=50, W=140, Cout=16, pool_k=6, pool_stride=6),
+    dict(N=1, Cin=7, H=40, W=60, Cout=16, pool_k=7, pool_stride=7),
+    dict(N=1, Cin=8, H=42, W=300, Cout=16, pool_k=8, pool_stride=8),
+    dict(N=1, Cin=8, H=30, W=30, Cout=16, scale=-1.5),      # window minimum
+    dict(N=1, Cin=8, H=30, W=30, Cout=16, scale=0.0),       # result is bias2
+    dict(N=1, Cin=8, H=30, W=30, Cout=16, conv_bias=False),
+    dict(N=1, Cin=1, H=6, W=6, Cout=1),                     # one pooled output
+]
+
+
+@pytest.mark.parametrize("kw", CONV_CASES)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_conv_pool_small(dev, kw, dtype):
+    c = inputgen.random_conv_case(3000, dtype=dtype, **kw)
+    _say("conv_pool", dtype, kw, "seed 3000")
+    ref = oracle.conv_tanh_scale_bias_maxpool(c)
+    got = _run_conv(c, dev)
+    assert not np.isnan(got).any()
+    tol = BF16_TOL if dtype == "bf16" else F32_TOL
+    np.testing.assert_allclose(got, ref, rtol=0, atol=tol)
+
+
+def test_conv_tiny_workload(dev):
+    c = inputgen.workload("tiny_conv")
+    _say("tiny_conv workload")
+    ref = oracle.conv_tanh_scale_bias_maxpool(c)
+    got = _run_conv(c, dev)
+    assert got.shape == (2, 16, 7, 7)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=F32_TOL)
+
+
+def _sample_idx(shape, n, seed):
+    total = int(np.prod(shape))
+    rng = np.random.default_rng(seed)
+    idx = rng.choice(total, size=min(n, total), replace=False)
+    # plus the corners of every (n, c) plane of the first and last image
+    N, C, PH, PW = shape
+    extra = []
+    for nn in (0, N - 1):
+        for cc in range(C):
+            base = (nn * C + cc) * PH * PW
+            extra += [base, base + PW - 1, base + (PH - 1) * PW, base + PH * PW - 1]
+    return np.unique(np.concatenate([idx, np.array(extra, dtype=np.int64)]))
+
+
+@pytest.mark.parametrize("name,tol", [("conv", F32_TOL), ("conv_bf16", BF16_TOL)])
+def test_conv_full_workload_sampled(dev, name, tol):
+    c = inputgen.workload(name)
+    _say(name, "workload", c["x"].shape)
+    got = _run_conv(c, dev)
+    assert got.shape == (128, 64, 63, 63)
+    assert not np.isnan(got).any()
+    idx = _sample_idx(got.shape, 40000, 5)
+    ref = oracle.conv_tanh_scale_bias_maxpool_points(c, idx)
+    np.testing.assert_allclose(got.ravel()[idx], ref, rtol=0, atol=tol)
+    # the first image in full
+    c1 = dict(c)
+    c1["x"] = c["x"][:1]
+    c1["N"] = 1
+    ref1 = oracle.conv_tanh_scale_bias_maxpool(c1)
+    np.testing.assert_allclose(got[:1], ref1, rtol=0, atol=tol)
+
+
+# ------------------------------------------------ convT + channel softmax ---
+def _run_convT(c, dev):
+    import pool_stencil_amd as ps
+    import torch
+    xd, wd = _dev(c["x"], dev), _dev(c["w"], dev)
+    cb = None if c["convT_bias"] is None else _dev(c["convT_bias"], dev)
+    b2 = _dev(c["bias2"], dev)
+    out = _canary(oracle.convT_out_shape(c), dev, torch.float32)
+    ps.convT_softmax_bias_scale_sigmoid(xd, wd, cb, b2, c["scale"], c["stride"], c["pad"],
+                                        c["output_padding"], c["dil"], out=out)
+    return out.cpu().numpy()
+
+
+CONVT_CASES = [
+    dict(N=2, Cin=64, H=9, W=7, Cout=128),
+    dict(N=1, Cin=64, H=16, W=16, Cout=128, output_padding=0),
+    dict(N=3, Cin=13, H=5, W=11, Cout=48),
+    dict(N=1, Cin=4, H=3, W=3, Cout=16),
+    dict(N=1, Cin=1, H=1, W=1, Cout=16),
+    dict(N=2, Cin=64, H=8, W=8, Cout=128, scale=-0.5, convT_bias=False),
+    dict(N=1, Cin=32, H=12, W=20, Cout=112),
+]
+
+
+@pytest.mark.parametrize("kw", CONVT_CASES)
+def test_convT_small(dev, kw):
+    c = inputgen.random_convT_case(4000, **kw)
+    _say("convT", kw, "seed 4000")
+    ref = oracle.convT_softmax_bias_scale_sigmoid(c)
+    got = _run_convT(c, dev)
+    assert not np.isnan(got).any()
+    np.testing.assert_allclose(got, ref, rtol=0, atol=F32_TOL)
+
+
+def test_convT_full_workload_sampled(dev):
+    c = inputgen.workload("convT")
+    _say("convT workload", c["x"].shape)
+    got = _run_convT(c, dev)
+    N, C, OH, OW = got.shape
+    assert (N, C, OH, OW) == (128, 128, 129, 129)
+    assert not np.isnan(got).any()
+    rng = np.random.default_rng(11)
+    pix = rng.choice(N * OH * OW, size=600, replace=False)
+    # boundary rows/columns 0 and 128 (the output_padding row) of a few images
+    edge = []
+    for n in (0, 77, 127):
+        for oh in (0, 1, 127, 128):
+            for ow in (0, 1, 64, 127, 128):
+                edge.append((n * OH + oh) * OW + ow)
+    pix = np.unique(np.concatenate([pix, np.array(edge, dtype=np.int64)]))
+    ref = oracle.convT_softmax_bias_scale_sigmoid_pixels(c, pix)
+    flat = got.transpose(0, 2, 3, 1).reshape(-1, C)
+    np.testing.assert_allclose(flat[pix], ref, rtol=0, atol=F32_TOL)
+    # softmax invariant on every pixel: sum_c (logit(y_c)/scale - bias2_c) == 1
+    g = got[:4].astype(np.float64)
+    sm = np.log(g / (1.0 - g)) / c["scale"] - c["bias2"].astype(np.float64).reshape(1, -1, 1, 1)
+    np.testing.assert_allclose(sm.sum(axis=1), 1.0, atol=5e-3)
