@@ -38,6 +38,11 @@ class PsError(RuntimeError):
 
 
 def _load() -> ctypes.CDLL:
+    # torch ships its own HIP runtime (libamdhip64).  Importing torch first makes the
+    # dynamic loader resolve the library's libamdhip64.so.7 dependency to that same
+    # runtime; loading the library first would map a second, independent runtime that
+    # cannot see torch's allocations or streams.
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is missing: build it with `python -m pool_stencil_amd.build` "

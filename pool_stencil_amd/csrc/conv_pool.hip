@@ -77,40 +77,21 @@ __global__ __launch_bounds__(64 * NPW) void conv_pool_f32(
     constexpr int PS = pad_words_16mod64(G::ROWS * G::RS);  // words per input channel
     constexpr int CINP = 4 * CING;
     __shared__ float tile[CINP * PS];
+    __shared__ float s_bias[2][64];  // conv bias, bias2 of the current 64-channel tile
 
     const uint32_t L = xcd_remap(blockIdx.x, gridDim.x);
     const int pwt = (int)(L % (uint32_t)npwt);
     const int ph = (int)((L / (uint32_t)npwt) % (uint32_t)PH);
     const int n = (int)(L / ((uint32_t)npwt * (uint32_t)PH));
 
-    // ---- stage the zero-padded halo tile ----
-    const int ir0 = PK * ph - pad;
-    const int ic0 = PK * pwt * G::T - pad;
-    const float *xn = x + (size_t)n * Cin * H * W;
-    for (int e = threadIdx.x; e < CINP * G::ROWS * G::COLS; e += 64 * NPW) {
-        const int c = e % G::COLS;
-        const int t = e / G::COLS;
-        const int r = t % G::ROWS;
-        const int ci = t / G::ROWS;
-        const int ir = ir0 + r, ic = ic0 + c;
-        float v = 0.f;
-        if (ci < Cin && ir >= 0 && ir < H && ic >= 0 && ic < W)
-            v = xn[((size_t)ci * H + ir) * W + ic];
-        tile[ci * PS + r * G::RS + (c % PK) * G::Q + c / PK] = v;
-    }
-    __syncthreads();
-
     const int lane = threadIdx.x & 63;
     const int wv = threadIdx.x >> 6;
     const int j = lane & 15;  // pooled column within the 16-wide group (B/D column)
     const int g4 = lane >> 4; // lane group: input channel within a K-step; D row block
-    const int pw = pwt * G::T + 16 * wv + j;
-    const float *tb = tile + g4 * PS + 16 * wv + j;
-    const float sgn = scale < 0.f ? -1.f : 1.f;
 
-    for (int ct = 0; ct < Cout; ct += 64) {
-        // A operands: w[co = ct + 16*nt + j][ci = 4*g + g4][tap]
-        float wr[4][9][CING];
+    // A operands of channel tile ct: w[co = ct + 16*nt + j][ci = 4*g + g4][tap]
+    float wr[4][9][CING];
+    auto load_weights = [&](int ct) {
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
             const int co = ct + 16 * nt + j;
@@ -118,12 +99,92 @@ __global__ __launch_bounds__(64 * NPW) void conv_pool_f32(
             for (int g = 0; g < CING; ++g) {
                 const int ci = 4 * g + g4;
                 const bool ok = co < Cout && ci < Cin;
-                const float *wp = w + ((size_t)co * Cin + ci) * 9;
+                const float *wp = w + ((size_t)(ok ? co : 0) * Cin + (ok ? ci : 0)) * 9;
 #pragma unroll
-                for (int tap = 0; tap < 9; ++tap) wr[nt][tap][g] = ok ? wp[tap] : 0.f;
+                for (int tap = 0; tap < 9; ++tap) {
+                    const float v = wp[tap];
+                    wr[nt][tap][g] = ok ? v : 0.f;
+                }
             }
         }
+    };
+    auto stage_bias = [&](int ct) {
+        if (threadIdx.x < 64) {
+            const int co = ct + threadIdx.x;
+            s_bias[0][threadIdx.x] = (co < Cout && cb) ? cb[co] : 0.f;
+            s_bias[1][threadIdx.x] = co < Cout ? b2[co] : 0.f;
+        }
+    };
+    // first tile's weights and biases: in flight together with the halo loads
+    load_weights(0);
+    stage_bias(0);
 
+    // ---- stage the zero-padded halo tile ----
+    // Every thread first issues all of its global loads (16-byte vectors when the
+    // tile's columns are 16-byte aligned), then writes them to LDS, so the loads
+    // of the whole tile are in flight together.
+    const int ir0 = PK * ph - pad;
+    const int ic0 = PK * pwt * G::T - pad;
+    const float *xn = x + (size_t)n * Cin * H * W;
+    {
+        constexpr int NT = 64 * NPW;
+        constexpr int NV = (G::COLS + 3) / 4;           // 4-column groups per tile row
+        constexpr int TOTAL = CINP * G::ROWS * NV;
+        constexpr int PER = (TOTAL + NT - 1) / NT;
+        const bool vec = ((ic0 & 3) == 0) && ((W & 3) == 0);
+        float4 buf[PER];
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int e = threadIdx.x + i * NT;
+            const int u = e % NV;
+            const int row = e / NV;
+            const int r = row % G::ROWS;
+            const int ci = row / G::ROWS;
+            const int ir = ir0 + r, ic = ic0 + 4 * u;
+            const bool rok = e < TOTAL && ci < Cin && ir >= 0 && ir < H;
+            const float *src = xn + ((size_t)ci * H + ir) * W + ic;
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (vec) {
+                if (rok && ic >= 0 && ic < W) v = *(const float4 *)src;
+            } else if (rok) {
+                if (ic >= 0 && ic < W) v.x = src[0];
+                if (ic + 1 >= 0 && ic + 1 < W) v.y = src[1];
+                if (ic + 2 >= 0 && ic + 2 < W) v.z = src[2];
+                if (ic + 3 >= 0 && ic + 3 < W) v.w = src[3];
+            }
+            buf[i] = v;
+        }
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int e = threadIdx.x + i * NT;
+            if (e < TOTAL) {
+                const int u = e % NV;
+                const int row = e / NV;
+                const int r = row % G::ROWS;
+                const int ci = row / G::ROWS;
+                float *trow = tile + ci * PS + r * G::RS;
+                const float vv[4] = {buf[i].x, buf[i].y, buf[i].z, buf[i].w};
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int c = 4 * u + k;
+                    if (c < G::COLS) trow[(c % PK) * G::Q + c / PK] = vv[k];
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    const int pw = pwt * G::T + 16 * wv + j;
+    const float *tb = tile + g4 * PS + 16 * wv + j;
+    const float sgn = scale < 0.f ? -1.f : 1.f;
+
+    for (int ct = 0; ct < Cout; ct += 64) {
+        if (ct > 0) {
+            __syncthreads();  // every wave is done with the previous tile's biases
+            stage_bias(ct);
+            load_weights(ct);
+            __syncthreads();
+        }
         f32x4 best[4];
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) best[nt] = (f32x4){-INFINITY, -INFINITY, -INFINITY, -INFINITY};
@@ -162,10 +223,12 @@ __global__ __launch_bounds__(64 * NPW) void conv_pool_f32(
             for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int co = ct + 16 * nt + 4 * g4 + r;
+                    const int cl = 16 * nt + 4 * g4 + r;
+                    const int co = ct + cl;
                     if (co < Cout) {
-                        const float v = sgn * best[nt][r] + (cb ? cb[co] : 0.f);
-                        y[(((size_t)n * Cout + co) * PH + ph) * PW + pw] = tanhf(v) * scale + b2[co];
+                        const float v = sgn * best[nt][r] + s_bias[0][cl];
+                        y[(((size_t)n * Cout + co) * PH + ph) * PW + pw] =
+                            tanhf(v) * scale + s_bias[1][cl];
                     }
                 }
         }
@@ -181,42 +244,112 @@ __global__ __launch_bounds__(64 * NPW) void conv_pool_bf16(
     using G = TileGeom<PK, NPW>;
     // channel-last tile: entry (row, plane, q) = 8 input channels as 8 bf16
     __shared__ uint4 tile[G::ROWS * G::RS];
+    __shared__ float s_bias[2][64];  // conv bias, bias2 of the current 64-channel tile
 
     const uint32_t L = xcd_remap(blockIdx.x, gridDim.x);
     const int pwt = (int)(L % (uint32_t)npwt);
     const int ph = (int)((L / (uint32_t)npwt) % (uint32_t)PH);
     const int n = (int)(L / ((uint32_t)npwt * (uint32_t)PH));
 
-    const int ir0 = PK * ph - pad;
-    const int ic0 = PK * pwt * G::T - pad;
-    const uint16_t *xn = x + (size_t)n * Cin * H * W;
-    const size_t cstride = (size_t)H * W;
-    for (int e = threadIdx.x; e < G::ROWS * G::COLS; e += 64 * NPW) {
-        const int c = e % G::COLS;
-        const int r = e / G::COLS;
-        const int ir = ir0 + r, ic = ic0 + c;
-        uint32_t h[8];
-#pragma unroll
-        for (int ci = 0; ci < 8; ++ci) h[ci] = 0;
-        if (ir >= 0 && ir < H && ic >= 0 && ic < W) {
-            const uint16_t *p = xn + (size_t)ir * W + ic;
-#pragma unroll
-            for (int ci = 0; ci < 8; ++ci)
-                if (ci < Cin) h[ci] = p[ci * cstride];
-        }
-        uint4 v;
-        v.x = h[0] | (h[1] << 16);
-        v.y = h[2] | (h[3] << 16);
-        v.z = h[4] | (h[5] << 16);
-        v.w = h[6] | (h[7] << 16);
-        tile[r * G::RS + (c % PK) * G::Q + c / PK] = v;
-    }
-    __syncthreads();
-
     const int lane = threadIdx.x & 63;
     const int wv = threadIdx.x >> 6;
     const int j = lane & 15;
     const int g4 = lane >> 4;
+
+    // A operands of channel tile ct: lane holds w[co = ct + 16*nt + j][ci = 0..7][tap = 4*s + g4]
+    bf16x8 wa[4][3];
+    auto load_weights = [&](int ct) {
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+            const int co = ct + 16 * nt + j;
+#pragma unroll
+            for (int s = 0; s < 3; ++s) {
+                const int tap = 4 * s + g4;
+                uint32_t hv[8];
+#pragma unroll
+                for (int ci = 0; ci < 8; ++ci) {
+                    const bool ok = co < Cout && ci < Cin && tap < 9;
+                    const uint32_t v = w[ok ? ((size_t)co * Cin + ci) * 9 + tap : 0];
+                    hv[ci] = ok ? v : 0u;
+                }
+                uint4 pk;
+                pk.x = hv[0] | (hv[1] << 16);
+                pk.y = hv[2] | (hv[3] << 16);
+                pk.z = hv[4] | (hv[5] << 16);
+                pk.w = hv[6] | (hv[7] << 16);
+                wa[nt][s] = __builtin_bit_cast(bf16x8, pk);
+            }
+        }
+    };
+    auto stage_bias = [&](int ct) {
+        if (threadIdx.x < 64) {
+            const int co = ct + threadIdx.x;
+            s_bias[0][threadIdx.x] = (co < Cout && cb) ? cb[co] : 0.f;
+            s_bias[1][threadIdx.x] = co < Cout ? b2[co] : 0.f;
+        }
+    };
+    load_weights(0);
+    stage_bias(0);
+
+    // ---- stage the tile channel-last: entry (row, column) = 8 channels ----
+    // A thread owns 8 consecutive columns of one row: it loads them for each of
+    // the 8 channels (one 16-byte load per channel when aligned), transposes the
+    // 8x8 block of bf16 in registers and writes 8 16-byte LDS entries.
+    const int ir0 = PK * ph - pad;
+    const int ic0 = PK * pwt * G::T - pad;
+    const uint16_t *xn = x + (size_t)n * Cin * H * W;
+    const size_t cstride = (size_t)H * W;
+    {
+        constexpr int NT = 64 * NPW;
+        constexpr int NG = (G::COLS + 7) / 8;   // 8-column groups per tile row
+        constexpr int TOTAL = G::ROWS * NG;
+        constexpr int PER = (TOTAL + NT - 1) / NT;
+        const bool vec = ((ic0 & 7) == 0) && ((W & 7) == 0);
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int e = threadIdx.x + i * NT;
+            const int u = e % NG;
+            const int r = e / NG;
+            const int ir = ir0 + r, ic = ic0 + 8 * u;
+            const bool rok = e < TOTAL && ir >= 0 && ir < H;
+            uint4 v[8];
+#pragma unroll
+            for (int ci = 0; ci < 8; ++ci) {
+                v[ci] = make_uint4(0u, 0u, 0u, 0u);
+                const uint16_t *src = xn + ci * cstride + (size_t)ir * W + ic;
+                if (vec) {
+                    if (rok && ci < Cin && ic >= 0 && ic < W) v[ci] = *(const uint4 *)src;
+                } else if (rok && ci < Cin) {
+                    uint32_t hv[8];
+#pragma unroll
+                    for (int k = 0; k < 8; ++k)
+                        hv[k] = (ic + k >= 0 && ic + k < W) ? (uint32_t)src[k] : 0u;
+                    v[ci] = make_uint4(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16),
+                                       hv[4] | (hv[5] << 16), hv[6] | (hv[7] << 16));
+                }
+            }
+            if (e < TOTAL) {
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const int c = 8 * u + k;
+                    // column k of channel ci: 16-bit half (k & 1) of word k / 2
+                    uint32_t h[8];
+#pragma unroll
+                    for (int ci = 0; ci < 8; ++ci) {
+                        const uint32_t wd = (k >> 1) == 0 ? v[ci].x : (k >> 1) == 1 ? v[ci].y
+                                          : (k >> 1) == 2 ? v[ci].z : v[ci].w;
+                        h[ci] = (k & 1) ? (wd >> 16) : (wd & 0xffffu);
+                    }
+                    if (c < G::COLS)
+                        tile[r * G::RS + (c % PK) * G::Q + c / PK] =
+                            make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16),
+                                       h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+                }
+            }
+        }
+    }
+    __syncthreads();
+
     const int pw = pwt * G::T + 16 * wv + j;
     const float sgn = scale < 0.f ? -1.f : 1.f;
 
@@ -235,26 +368,11 @@ __global__ __launch_bounds__(64 * NPW) void conv_pool_bf16(
     }
 
     for (int ct = 0; ct < Cout; ct += 64) {
-        // A operands: lane holds w[co = ct + 16*nt + j][ci = 0..7][tap = 4*s + g4]
-        bf16x8 wa[4][3];
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-            const int co = ct + 16 * nt + j;
-#pragma unroll
-            for (int s = 0; s < 3; ++s) {
-                const int tap = 4 * s + g4;
-                uint32_t hv[8];
-#pragma unroll
-                for (int ci = 0; ci < 8; ++ci)
-                    hv[ci] = (co < Cout && ci < Cin && tap < 9) ? (uint32_t)w[((size_t)co * Cin + ci) * 9 + tap]
-                                                                : 0u;
-                uint4 pk;
-                pk.x = hv[0] | (hv[1] << 16);
-                pk.y = hv[2] | (hv[3] << 16);
-                pk.z = hv[4] | (hv[5] << 16);
-                pk.w = hv[6] | (hv[7] << 16);
-                wa[nt][s] = __builtin_bit_cast(bf16x8, pk);
-            }
+        if (ct > 0) {
+            __syncthreads();  // every wave is done with the previous tile's biases
+            stage_bias(ct);
+            load_weights(ct);
+            __syncthreads();
         }
 
         f32x4 best[4];
@@ -289,11 +407,12 @@ __global__ __launch_bounds__(64 * NPW) void conv_pool_bf16(
             for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int co = ct + 16 * nt + 4 * g4 + r;
+                    const int cl = 16 * nt + 4 * g4 + r;
+                    const int co = ct + cl;
                     if (co < Cout) {
-                        const float v = sgn * best[nt][r] + (cb ? cb[co] : 0.f);
+                        const float v = sgn * best[nt][r] + s_bias[0][cl];
                         y[(((size_t)n * Cout + co) * PH + ph) * PW + pw] =
-                            f32_to_bf16_rne(tanhf(v) * scale + b2[co]);
+                            f32_to_bf16_rne(tanhf(v) * scale + s_bias[1][cl]);
                     }
                 }
         }

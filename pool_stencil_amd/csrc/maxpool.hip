@@ -36,6 +36,18 @@ namespace {
 
 constexpr int kWave = 64;
 
+// Tuning knobs (compile-time): rows of loads in flight per wave, output rows
+// per band, and whether outputs are stored with the nontemporal hint.
+#ifndef PS_MAXPOOL_PREFETCH
+#define PS_MAXPOOL_PREFETCH 3
+#endif
+#ifndef PS_MAXPOOL_BAND_ROWS
+#define PS_MAXPOOL_BAND_ROWS 32
+#endif
+#ifndef PS_MAXPOOL_NT_STORE
+#define PS_MAXPOOL_NT_STORE 0
+#endif
+
 __device__ __forceinline__ float rot_lanes(float v, int src_lane_x4) {
     return __int_as_float(__builtin_amdgcn_ds_bpermute(src_lane_x4, __float_as_int(v)));
 }
@@ -59,7 +71,7 @@ __device__ __forceinline__ void widen(float (&v)[V + 1], int lane, int shift) {
     v[V] = fmax_ordered(v[V], rot[V]);
 }
 
-template <int K, int V>
+template <int K, int V, int PF>
 __global__ __launch_bounds__(256) void maxpool_s1_rows(
     const float *__restrict__ x, float *__restrict__ y, int H, int W, int OH, int OW, int pad,
     int band_rows, int nbands, int nstrips, uint64_t ntasks) {
@@ -98,53 +110,69 @@ __global__ __launch_bounds__(256) void maxpool_s1_rows(
             v[j] = (rowok && colok[j]) ? rp[kWave * j] : -INFINITY;
     };
 
+    // PF input rows are in flight at any time: slot s of `pf` holds row
+    // ih_first + base + s; after a row is consumed its slot is refilled with the
+    // row PF further down.  The slot loop is unrolled, so every register index is
+    // static and no pending load is ever copied.
+    const int nrows = ih_last - ih_first + 1;
+    float pf[PF][V + 1];
+#pragma unroll
+    for (int s = 0; s < PF; ++s)
+        if (s < nrows) load_row(ih_first + s, pf[s]);
+
     float ring[K][V];
-    float nxt[V + 1];
-    load_row(ih_first, nxt);
-    int ih = ih_first;
-    for (int r = 0; ih <= ih_last; ++r, ++ih) {
-        float v[V + 1];
+    for (int base = 0; base < nrows; base += PF) {
 #pragma unroll
-        for (int j = 0; j <= V; ++j) v[j] = nxt[j];
-        if (ih < ih_last) load_row(ih + 1, nxt);  // one row of prefetch in flight
+        for (int s = 0; s < PF; ++s) {
+            const int r = base + s;
+            if (r >= nrows) break;
+            const int ih = ih_first + r;
+            float v[V + 1];
+#pragma unroll
+            for (int j = 0; j <= V; ++j) v[j] = pf[s][j];
+            if (r + PF < nrows) load_row(ih + PF, pf[s]);
 
-        // horizontal window-K max by doubling: window 1 -> 2 -> 4 (-> 8)
-        constexpr int P = K >= 8 ? 8 : K >= 4 ? 4 : K >= 2 ? 2 : 1;  // largest power of 2 <= K
-        if constexpr (P >= 2) widen<V>(v, lane, 1);
-        if constexpr (P >= 4) widen<V>(v, lane, 2);
-        if constexpr (P >= 8) widen<V>(v, lane, 4);
-        if constexpr (K != P) {
-            // window K = window P at c  combined with window P at c + (K - P)
-            float w2[V + 1];
+            // horizontal window-K max by doubling: window 1 -> 2 -> 4 (-> 8)
+            constexpr int P = K >= 8 ? 8 : K >= 4 ? 4 : K >= 2 ? 2 : 1;  // largest power of 2 <= K
+            if constexpr (P >= 2) widen<V>(v, lane, 1);
+            if constexpr (P >= 4) widen<V>(v, lane, 2);
+            if constexpr (P >= 8) widen<V>(v, lane, 4);
+            if constexpr (K != P) {
+                // window K = window P at c  combined with window P at c + (K - P)
+                const int sh = K - P;
+                const int src = ((lane + sh) & (kWave - 1)) << 2;
+                const bool carry = lane + sh >= kWave;
+                float rot[V + 1];
 #pragma unroll
-            for (int j = 0; j <= V; ++j) w2[j] = v[j];
-            const int sh = K - P;
-            const int src = ((lane + sh) & (kWave - 1)) << 2;
-            const bool carry = lane + sh >= kWave;
-            float rot[V + 1];
+                for (int j = 0; j <= V; ++j) rot[j] = rot_lanes(v[j], src);
 #pragma unroll
-            for (int j = 0; j <= V; ++j) rot[j] = rot_lanes(w2[j], src);
-#pragma unroll
-            for (int j = 0; j < V; ++j) v[j] = fmax_ordered(v[j], carry ? rot[j + 1] : rot[j]);
-        }
+                for (int j = 0; j < V; ++j) v[j] = fmax_ordered(v[j], carry ? rot[j + 1] : rot[j]);
+            }
 
-        // shift the vertical ring and append this row's horizontal maxima
+            // shift the vertical ring and append this row's horizontal maxima
 #pragma unroll
-        for (int i = 0; i < K - 1; ++i)
+            for (int i = 0; i < K - 1; ++i)
 #pragma unroll
-            for (int j = 0; j < V; ++j) ring[i][j] = ring[i + 1][j];
+                for (int j = 0; j < V; ++j) ring[i][j] = ring[i + 1][j];
 #pragma unroll
-        for (int j = 0; j < V; ++j) ring[K - 1][j] = v[j];
+            for (int j = 0; j < V; ++j) ring[K - 1][j] = v[j];
 
-        if (r >= K - 1) {
-            const int oh = ih - (K - 1) + pad;
-            float *orow = yp + (int64_t)oh * OW + c0 + lane;
+            if (r >= K - 1) {
+                const int oh = ih - (K - 1) + pad;
+                float *orow = yp + (int64_t)oh * OW + c0 + lane;
 #pragma unroll
-            for (int j = 0; j < V; ++j) {
-                float m = ring[0][j];
+                for (int j = 0; j < V; ++j) {
+                    float m = ring[0][j];
 #pragma unroll
-                for (int i = 1; i < K; ++i) m = fmax_ordered(m, ring[i][j]);
-                if (c0 + kWave * j + lane < OW) orow[kWave * j] = m;
+                    for (int i = 1; i < K; ++i) m = fmax_ordered(m, ring[i][j]);
+                    if (c0 + kWave * j + lane < OW) {
+#if PS_MAXPOOL_NT_STORE
+                        __builtin_nontemporal_store(m, orow + kWave * j);
+#else
+                        orow[kWave * j] = m;
+#endif
+                    }
+                }
             }
         }
     }
@@ -176,13 +204,13 @@ __global__ __launch_bounds__(256) void maxpool_direct(const float *__restrict__ 
 template <int K, int V>
 int launch_rows(const float *x, float *y, int N, int C, int H, int W, int OH, int OW, int p,
                 hipStream_t stream) {
-    const int band_rows = 32;
+    const int band_rows = PS_MAXPOOL_BAND_ROWS;
     const int nbands = (OH + band_rows - 1) / band_rows;
     const int nstrips = (OW + kWave * V - 1) / (kWave * V);
     const uint64_t ntasks = (uint64_t)N * C * nstrips * nbands;
     const uint64_t nblocks = (ntasks + 3) / 4;
     if (nblocks > 0x7fffffffull) return PS_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL((maxpool_s1_rows<K, V>), dim3((unsigned)nblocks), dim3(256), 0, stream,
+    hipLaunchKernelGGL((maxpool_s1_rows<K, V, PS_MAXPOOL_PREFETCH>), dim3((unsigned)nblocks), dim3(256), 0, stream,
                        x, y, H, W, OH, OW, p, band_rows, nbands, nstrips, ntasks);
     return hipGetLastError() == hipSuccess ? PS_OK : PS_ERR_HIP;
 }
