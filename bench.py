@@ -39,9 +39,39 @@ POOL_BYTES = 32 * 64 * 512 * 512 * 4 + 32 * 64 * 511 * 511 * 4
 CONVT_FLOP = 2 * 128 * 64 * 128 * 255 * 255
 CONVT_BYTES = 128 * 64 * 64 * 64 * 4 + 128 * 128 * 129 * 129 * 4 + 64 * 128 * 16 * 4
 
-# HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE (profiles/), scaled
-# by the copy-kernel calibration factor; None until measured for the current kernels.
-TRAFFIC = {"conv": None, "maxpool": None, "convT": None, "conv_bf16": None}
+# HBM bytes per launch, from two rocprofv3 --pmc passes over this script (FETCH_SIZE,
+# then WRITE_SIZE, KiB per dispatch), each scaled by what the same counter reads for a
+# device copy of known size (`bench.py --copy-calibration`): FETCH_SIZE x2.0, WRITE_SIZE
+# x1.0.  `src` is the hash of the kernel's sources when the counters were taken; a
+# kernel edited since then reports traffic null.  See profiles/traffic_*.md.
+TRAFFIC = {
+    "conv": {"src": "9d88e62625fff3d6", "fetch_bytes": 266808402, "write_bytes": 130671872},
+    "maxpool": {"src": "231157ba21664983", "fetch_bytes": 2336400059, "write_bytes": 2141036064},
+    "convT": {"src": "4756821d0a67bf5e", "fetch_bytes": 756798175, "write_bytes": 2829362368},
+    "conv_bf16": {"src": "9d88e62625fff3d6", "fetch_bytes": 133664294, "write_bytes": 65041600},
+}
+KERNEL_SOURCES = {
+    "conv": ["conv_pool.hip", "ps_internal.h"],
+    "conv_bf16": ["conv_pool.hip", "ps_internal.h"],
+    "maxpool": ["maxpool.hip", "ps_internal.h"],
+    "convT": ["convt_softmax.hip", "ps_internal.h"],
+}
+
+
+def source_hash(op):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[op]:
+        with open(os.path.join(ROOT, "pool_stencil_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic(op):
+    t = TRAFFIC.get(op)
+    if not t or t["src"] != source_hash(op):
+        return None
+    return t["fetch_bytes"] + t["write_bytes"]
 
 
 def parse():
@@ -52,7 +82,29 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (profiling runs)")
     ap.add_argument("--ops", default="conv,maxpool,convT,conv_bf16")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="time a 2 GiB device-to-device copy instead (counter calibration)")
     return ap.parse_args()
+
+
+def copy_calibration(steps):
+    """A plain device copy of known size: 2 GiB read + 2 GiB written per launch."""
+    import torch
+    n = 32 * 64 * 512 * 512
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        y.copy_(x)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    print(json.dumps({"copy_calibration": True, "bytes_read": n * 4, "bytes_written": n * 4,
+                      "ms": ms, "GBps": 2 * n * 4 / ms / 1e6}), flush=True)
 
 
 def main():
@@ -63,6 +115,10 @@ def main():
               "the operations shard over the batch with no communication, so the one-GPU "
               "figure is the per-GPU figure", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration(args.steps)
+        return
 
     import numpy as np
     import torch
@@ -155,7 +211,7 @@ def main():
             "gflop_per_launch": CONV_FLOP / 1e9,
             "value_page_count": CONV_FLOP_PAGE / (mean * 1e-3) / 1e9,
             "roofline": {"bound": "mfma", "achieved": ach / 1e12, "peak": PEAK_FP32 / 1e12,
-                         "unit": "TFLOP/s", "frac": ach / PEAK_FP32, "traffic": TRAFFIC["conv"]}}
+                         "unit": "TFLOP/s", "frac": ach / PEAK_FP32, "traffic": traffic("conv")}}
     if "maxpool" in runs:
         mean, med, mn = stats("maxpool")
         ach = POOL_BYTES / (mean * 1e-3)
@@ -163,7 +219,7 @@ def main():
             "value": ach / 1e9, "unit": "GB/s", "ms_mean": mean, "ms_median": med, "ms_min": mn,
             "gbytes_per_launch": POOL_BYTES / 1e9,
             "roofline": {"bound": "hbm", "achieved": ach / 1e9, "peak": PEAK_HBM / 1e9,
-                         "unit": "GB/s", "frac": ach / PEAK_HBM, "traffic": TRAFFIC["maxpool"]}}
+                         "unit": "GB/s", "frac": ach / PEAK_HBM, "traffic": traffic("maxpool")}}
     if "convT" in runs:
         mean, med, mn = stats("convT")
         ach = CONVT_FLOP / (mean * 1e-3)
@@ -172,7 +228,7 @@ def main():
             "gflop_per_launch": CONVT_FLOP / 1e9,
             "hbm_GBps": CONVT_BYTES / (mean * 1e-3) / 1e9,
             "roofline": {"bound": "mfma", "achieved": ach / 1e12, "peak": PEAK_FP32 / 1e12,
-                         "unit": "TFLOP/s", "frac": ach / PEAK_FP32, "traffic": TRAFFIC["convT"]}}
+                         "unit": "TFLOP/s", "frac": ach / PEAK_FP32, "traffic": traffic("convT")}}
     if "conv_bf16" in runs:
         mean, med, mn = stats("conv_bf16")
         ach = CONV_FLOP / (mean * 1e-3)
@@ -180,7 +236,7 @@ def main():
             "value": ach / 1e9, "unit": "GFLOP/s", "ms_mean": mean, "ms_median": med, "ms_min": mn,
             "gflop_per_launch": CONV_FLOP / 1e9,
             "roofline": {"bound": "mfma", "achieved": ach / 1e12, "peak": PEAK_BF16 / 1e12,
-                         "unit": "TFLOP/s", "frac": ach / PEAK_BF16, "traffic": TRAFFIC["conv_bf16"],
+                         "unit": "TFLOP/s", "frac": ach / PEAK_BF16, "traffic": traffic("conv_bf16"),
                          "frac_of_fp32_peak": ach / PEAK_FP32}}
 
     head = "conv" if "conv" in out_ops else next(iter(out_ops))
@@ -223,7 +279,7 @@ def cpu_baseline():
     import oracle
     import inputgen
     c = inputgen.workload("conv")
-    n_img = int(os.environ.get("PS_CPU_IMAGES", "4"))
+    n_img = int(os.environ.get("PS_CPU_IMAGES", "128"))
     c1 = dict(c)
     c1["x"] = c["x"][:n_img]
     c1["N"] = n_img

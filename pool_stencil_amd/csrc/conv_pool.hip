@@ -68,8 +68,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
 // ---------------------------------------------------------------- fp32 ---
+#ifndef PS_CONV_MIN_WAVES
+#define PS_CONV_MIN_WAVES 1
+#endif
+
 template <int PK, int NPW, int CING>
-__global__ __launch_bounds__(64 * NPW) void conv_pool_f32(
+__global__ __launch_bounds__(64 * NPW, PS_CONV_MIN_WAVES) void conv_pool_f32(
     const float *__restrict__ x, const float *__restrict__ w, const float *__restrict__ cb,
     const float *__restrict__ b2, float *__restrict__ y, int Cin, int H, int W, int Cout,
     int pad, int PH, int PW, float scale, int npwt) {

@@ -125,19 +125,21 @@ __global__ __launch_bounds__(kThreads) void convT_softmax_f32(
 #pragma unroll
             for (int nq = 0; nq < NQ; ++nq) acc[mt][nq] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-        for (int cl = 0; cl < Cq; ++cl) {  // one input channel of this lane group
+        // B operands of input channel cl of this lane group: the 2x2 input
+        // neighbourhood of each pixel, (u,v) = (0,0) (0,1) (1,0) (1,1)
+        auto load_b = [&](int cl, float (&bv)[NQ][4]) {
             const bool ciok = G * Cq + cl < Cin;
-            float bv[NQ][4];
 #pragma unroll
             for (int nq = 0; nq < NQ; ++nq) {
                 const float *p = xb[nq] + (size_t)cl * plane;
                 const bool ok = ciok && pok[nq];
-                // s%4 = 2u + v : (u,v) = (0,0) (0,1) (1,0) (1,1)
                 bv[nq][0] = (ok && r0[nq] && c0[nq]) ? p[0] : 0.f;
                 bv[nq][1] = (ok && r0[nq] && c1[nq]) ? p[-1] : 0.f;
                 bv[nq][2] = (ok && r1[nq] && c0[nq]) ? p[-W] : 0.f;
                 bv[nq][3] = (ok && r1[nq] && c1[nq]) ? p[-W - 1] : 0.f;
             }
+        };
+        auto compute = [&](int cl, const float (&bv)[NQ][4]) {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 const f32x4 av = *(const f32x4 *)(aw + mt * 16 * CS + 4 * cl);
@@ -148,7 +150,19 @@ __global__ __launch_bounds__(kThreads) void convT_softmax_f32(
                         acc[mt][nq] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[tp], bv[nq][tp],
                                                                            acc[mt][nq], 0, 0, 0);
             }
+        };
+        // two channels per trip: the next channel's loads are in flight while the
+        // current one feeds the matrix cores
+        float bA[NQ][4], bB[NQ][4];
+        load_b(0, bA);
+        int cl = 0;
+        for (; cl + 1 < Cq; cl += 2) {
+            load_b(cl + 1, bB);
+            compute(cl, bA);
+            if (cl + 2 < Cq) load_b(cl + 2, bA);
+            compute(cl + 1, bB);
         }
+        if (cl < Cq) compute(cl, bA);
 
         // ---- epilogue: D row 4G + r of tile mt = channel 16mt + 4G + r ----
 #pragma unroll

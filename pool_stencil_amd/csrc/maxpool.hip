@@ -37,15 +37,25 @@ namespace {
 constexpr int kWave = 64;
 
 // Tuning knobs (compile-time): rows of loads in flight per wave, output rows
-// per band, and whether outputs are stored with the nontemporal hint.
+// per band, nontemporal hints on the output stores / input loads.
 #ifndef PS_MAXPOOL_PREFETCH
-#define PS_MAXPOOL_PREFETCH 3
+#define PS_MAXPOOL_PREFETCH 2
 #endif
 #ifndef PS_MAXPOOL_BAND_ROWS
 #define PS_MAXPOOL_BAND_ROWS 32
 #endif
 #ifndef PS_MAXPOOL_NT_STORE
 #define PS_MAXPOOL_NT_STORE 0
+#endif
+#ifndef PS_MAXPOOL_NT_LOAD
+#define PS_MAXPOOL_NT_LOAD 0
+#endif
+// Resident workgroups per CU (0 = as many as registers allow).  Fewer concurrent
+// row streams keep more DRAM pages open per stream: on MI355X three workgroups
+// (12 waves) per CU moved the k4 s1 p1 pool from 4.9 to 5.2 TB/s.  The cap is
+// applied by reserving a matching share of the CU's LDS for each workgroup.
+#ifndef PS_MAXPOOL_WGS_PER_CU
+#define PS_MAXPOOL_WGS_PER_CU 3
 #endif
 
 __device__ __forceinline__ float rot_lanes(float v, int src_lane_x4) {
@@ -107,7 +117,11 @@ __global__ __launch_bounds__(256) void maxpool_s1_rows(
         const float *rp = xp + (int64_t)ih * W + ic0 + lane;
 #pragma unroll
         for (int j = 0; j <= V; ++j)
+#if PS_MAXPOOL_NT_LOAD
+            v[j] = (rowok && colok[j]) ? __builtin_nontemporal_load(rp + kWave * j) : -INFINITY;
+#else
             v[j] = (rowok && colok[j]) ? rp[kWave * j] : -INFINITY;
+#endif
     };
 
     // PF input rows are in flight at any time: slot s of `pf` holds row
@@ -201,6 +215,18 @@ __global__ __launch_bounds__(256) void maxpool_direct(const float *__restrict__ 
     y[i] = m;
 }
 
+// Dynamic LDS bytes that leave room for exactly PS_MAXPOOL_WGS_PER_CU workgroups per CU.
+int occupancy_cap_lds_bytes() {
+    if (PS_MAXPOOL_WGS_PER_CU <= 0) return 0;
+    int dev = 0, lds = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
+        hipSuccess)
+        return 0;
+    const int share = lds / PS_MAXPOOL_WGS_PER_CU - 256;
+    return share > 0 && share <= 65536 ? share : 0;
+}
+
 template <int K, int V>
 int launch_rows(const float *x, float *y, int N, int C, int H, int W, int OH, int OW, int p,
                 hipStream_t stream) {
@@ -210,7 +236,8 @@ int launch_rows(const float *x, float *y, int N, int C, int H, int W, int OH, in
     const uint64_t ntasks = (uint64_t)N * C * nstrips * nbands;
     const uint64_t nblocks = (ntasks + 3) / 4;
     if (nblocks > 0x7fffffffull) return PS_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL((maxpool_s1_rows<K, V, PS_MAXPOOL_PREFETCH>), dim3((unsigned)nblocks), dim3(256), 0, stream,
+    hipLaunchKernelGGL((maxpool_s1_rows<K, V, PS_MAXPOOL_PREFETCH>), dim3((unsigned)nblocks), dim3(256),
+                       occupancy_cap_lds_bytes(), stream,
                        x, y, H, W, OH, OW, p, band_rows, nbands, nstrips, ntasks);
     return hipGetLastError() == hipSuccess ? PS_OK : PS_ERR_HIP;
 }
