@@ -45,10 +45,10 @@ CONVT_BYTES = 128 * 64 * 64 * 64 * 4 + 128 * 128 * 129 * 129 * 4 + 64 * 128 * 16
 # x1.0.  `src` is the hash of the kernel's sources when the counters were taken; a
 # kernel edited since then reports traffic null.  See profiles/traffic_*.md.
 TRAFFIC = {
-    "conv": {"src": "9d88e62625fff3d6", "fetch_bytes": 266808402, "write_bytes": 130671872},
-    "maxpool": {"src": "231157ba21664983", "fetch_bytes": 2336400059, "write_bytes": 2141036064},
-    "convT": {"src": "4756821d0a67bf5e", "fetch_bytes": 756798175, "write_bytes": 2829362368},
-    "conv_bf16": {"src": "9d88e62625fff3d6", "fetch_bytes": 133664294, "write_bytes": 65041600},
+    "conv": {"src": "f836461b7418e386", "fetch_bytes": 266806354, "write_bytes": 130668896},
+    "maxpool": {"src": "231157ba21664983", "fetch_bytes": 2336400059, "write_bytes": 2140966016},
+    "convT": {"src": "4756821d0a67bf5e", "fetch_bytes": 756348644, "write_bytes": 2830417056},
+    "conv_bf16": {"src": "f836461b7418e386", "fetch_bytes": 136834562, "write_bytes": 82845024},
 }
 KERNEL_SOURCES = {
     "conv": ["conv_pool.hip", "ps_internal.h"],

@@ -240,27 +240,83 @@ __global__ __launch_bounds__(64 * NPW, PS_CONV_MIN_WAVES) void conv_pool_f32(
 }
 
 // ---------------------------------------------------------------- bf16 ---
-template <int PK, int NPW>
-__global__ __launch_bounds__(64 * NPW) void conv_pool_bf16(
+// Persistent, software-pipelined: a workgroup owns a run of consecutive pooled
+// rows [p0, p1) of one image and one 16*NPW-column strip.  Its weights are loaded
+// once.  Input rows live in an LDS ring of 2*PK + 2 rows (channel-last entries of
+// 8 bf16): pooled row ph reads ring rows PK*ph - pad ... + PK + 1, while the PK
+// rows that pooled row ph+1 adds are loaded from HBM into registers during the
+// MFMA work of row ph and written to the ring afterwards.  One barrier per row.
+template <int PK, int NPW, bool VEC>
+__global__ __launch_bounds__(64 * NPW, 2) void conv_pool_bf16(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, const float *__restrict__ cb,
     const float *__restrict__ b2, uint16_t *__restrict__ y, int Cin, int H, int W, int Cout,
-    int pad, int PH, int PW, float scale, int npwt) {
+    int pad, int PH, int PW, float scale, int npwt, int nseg) {
     using G = TileGeom<PK, NPW>;
-    // channel-last tile: entry (row, plane, q) = 8 input channels as 8 bf16
-    __shared__ uint4 tile[G::ROWS * G::RS];
-    __shared__ float s_bias[2][64];  // conv bias, bias2 of the current 64-channel tile
+    constexpr int NT = 64 * NPW;
+    constexpr int RING = 2 * PK + 2;        // input rows held in LDS
+    constexpr int NG = (G::COLS + 7) / 8;   // 8-column groups per tile row
+    __shared__ uint4 ring[RING * G::RS];
+    __shared__ float s_bias[2][64];
 
+    // ---- work item: (image n, column strip pwt, pooled rows [p0, p1)) ----
     const uint32_t L = xcd_remap(blockIdx.x, gridDim.x);
-    const int pwt = (int)(L % (uint32_t)npwt);
-    const int ph = (int)((L / (uint32_t)npwt) % (uint32_t)PH);
-    const int n = (int)(L / ((uint32_t)npwt * (uint32_t)PH));
+    const int seg = (int)(L % (uint32_t)nseg);
+    const int pwt = (int)((L / (uint32_t)nseg) % (uint32_t)npwt);
+    const int n = (int)(L / ((uint32_t)nseg * (uint32_t)npwt));
+    const int p0 = (int)(((int64_t)PH * seg) / nseg);
+    const int p1 = (int)(((int64_t)PH * (seg + 1)) / nseg);
 
     const int lane = threadIdx.x & 63;
     const int wv = threadIdx.x >> 6;
     const int j = lane & 15;
     const int g4 = lane >> 4;
+    const int ic0 = PK * pwt * G::T - pad;
+    const uint16_t *xn = x + (size_t)n * Cin * H * W;
+    const size_t cstride = (size_t)H * W;
+    // VEC: the strip's columns are 16-byte aligned (ic0 % 8 == 0, W % 8 == 0), so a
+    // group of 8 columns is one 16-byte load per channel and lies wholly inside or
+    // wholly outside the image; otherwise columns are loaded one by one.
 
-    // A operands of channel tile ct: lane holds w[co = ct + 16*nt + j][ci = 0..7][tap = 4*s + g4]
+    // Load input row ir, columns [ic0 + 8u, ic0 + 8u + 8), all 8 channels.
+    auto load_group = [&](int ir, int u, uint4 (&v)[8]) {
+        const int ic = ic0 + 8 * u;
+        const bool rok = ir >= 0 && ir < H;
+#pragma unroll
+        for (int ci = 0; ci < 8; ++ci) {
+            v[ci] = make_uint4(0u, 0u, 0u, 0u);
+            const uint16_t *src = xn + ci * cstride + (size_t)ir * W + ic;
+            if constexpr (VEC) {
+                if (rok && ci < Cin && ic >= 0 && ic < W) v[ci] = *(const uint4 *)src;
+            } else if (rok && ci < Cin) {
+                uint32_t hv[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    hv[k] = (ic + k >= 0 && ic + k < W) ? (uint32_t)src[k] : 0u;
+                v[ci] = make_uint4(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16),
+                                   hv[4] | (hv[5] << 16), hv[6] | (hv[7] << 16));
+            }
+        }
+    };
+    // Transpose the 8x8 block (channel x column) and write 8 channel-last entries.
+    auto store_group = [&](int ir, int u, const uint4 (&v)[8]) {
+        uint4 *rrow = ring + (((ir % RING) + RING) % RING) * G::RS;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int c = 8 * u + k;
+            uint32_t h[8];
+#pragma unroll
+            for (int ci = 0; ci < 8; ++ci) {
+                const uint32_t wd = (k >> 1) == 0 ? v[ci].x : (k >> 1) == 1 ? v[ci].y
+                                  : (k >> 1) == 2 ? v[ci].z : v[ci].w;
+                h[ci] = (k & 1) ? (wd >> 16) : (wd & 0xffffu);
+            }
+            if (c < G::COLS)
+                rrow[(c % PK) * G::Q + c / PK] = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16),
+                                                           h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+        }
+    };
+
+    // A operands: lane holds w[co = ct + 16*nt + j][ci = 0..7][tap = 4*s + g4]
     bf16x8 wa[4][3];
     auto load_weights = [&](int ct) {
 #pragma unroll
@@ -292,134 +348,120 @@ __global__ __launch_bounds__(64 * NPW) void conv_pool_bf16(
             s_bias[1][threadIdx.x] = co < Cout ? b2[co] : 0.f;
         }
     };
-    load_weights(0);
-    stage_bias(0);
 
-    // ---- stage the tile channel-last: entry (row, column) = 8 channels ----
-    // A thread owns 8 consecutive columns of one row: it loads them for each of
-    // the 8 channels (one 16-byte load per channel when aligned), transposes the
-    // 8x8 block of bf16 in registers and writes 8 16-byte LDS entries.
-    const int ir0 = PK * ph - pad;
-    const int ic0 = PK * pwt * G::T - pad;
-    const uint16_t *xn = x + (size_t)n * Cin * H * W;
-    const size_t cstride = (size_t)H * W;
-    {
-        constexpr int NT = 64 * NPW;
-        constexpr int NG = (G::COLS + 7) / 8;   // 8-column groups per tile row
-        constexpr int TOTAL = G::ROWS * NG;
+    // ---- prologue: the PK + 2 input rows of pooled row p0 ----
+    if (p0 < p1) {
+        constexpr int TOTAL = (PK + 2) * NG;
         constexpr int PER = (TOTAL + NT - 1) / NT;
-        const bool vec = ((ic0 & 7) == 0) && ((W & 7) == 0);
+        const int ir0 = PK * p0 - pad;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int e = threadIdx.x + i * NT;
-            const int u = e % NG;
-            const int r = e / NG;
-            const int ir = ir0 + r, ic = ic0 + 8 * u;
-            const bool rok = e < TOTAL && ir >= 0 && ir < H;
-            uint4 v[8];
-#pragma unroll
-            for (int ci = 0; ci < 8; ++ci) {
-                v[ci] = make_uint4(0u, 0u, 0u, 0u);
-                const uint16_t *src = xn + ci * cstride + (size_t)ir * W + ic;
-                if (vec) {
-                    if (rok && ci < Cin && ic >= 0 && ic < W) v[ci] = *(const uint4 *)src;
-                } else if (rok && ci < Cin) {
-                    uint32_t hv[8];
-#pragma unroll
-                    for (int k = 0; k < 8; ++k)
-                        hv[k] = (ic + k >= 0 && ic + k < W) ? (uint32_t)src[k] : 0u;
-                    v[ci] = make_uint4(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16),
-                                       hv[4] | (hv[5] << 16), hv[6] | (hv[7] << 16));
-                }
-            }
             if (e < TOTAL) {
-#pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    const int c = 8 * u + k;
-                    // column k of channel ci: 16-bit half (k & 1) of word k / 2
-                    uint32_t h[8];
-#pragma unroll
-                    for (int ci = 0; ci < 8; ++ci) {
-                        const uint32_t wd = (k >> 1) == 0 ? v[ci].x : (k >> 1) == 1 ? v[ci].y
-                                          : (k >> 1) == 2 ? v[ci].z : v[ci].w;
-                        h[ci] = (k & 1) ? (wd >> 16) : (wd & 0xffffu);
-                    }
-                    if (c < G::COLS)
-                        tile[r * G::RS + (c % PK) * G::Q + c / PK] =
-                            make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16),
-                                       h[4] | (h[5] << 16), h[6] | (h[7] << 16));
-                }
+                uint4 v[8];
+                load_group(ir0 + e / NG, e % NG, v);
+                store_group(ir0 + e / NG, e % NG, v);
             }
         }
     }
-    __syncthreads();
-
-    const int pw = pwt * G::T + 16 * wv + j;
-    const float sgn = scale < 0.f ? -1.f : 1.f;
 
     // Per lane, K-step s covers kernel tap 4*s + g4 (taps >= 9 carry zero weights
-    // and read a valid in-tile entry).  LDS entry offsets for each (s, dx).
-    int off[3][PK];
+    // and read a valid in-ring entry).  Column part of the ring offset per (s, dx).
+    int coff[3][PK];
+    int khs[3];
 #pragma unroll
     for (int s = 0; s < 3; ++s) {
         const int tap = min(4 * s + g4, 8);
         const int kh = tap / 3, kw = tap % 3;
+        khs[s] = kh;
 #pragma unroll
         for (int dx = 0; dx < PK; ++dx) {
             const int t = dx + kw;
-            off[s][dx] = kh * G::RS + (t % PK) * G::Q + 16 * wv + j + t / PK;
+            coff[s][dx] = (t % PK) * G::Q + 16 * wv + j + t / PK;
         }
     }
+    const int pw = pwt * G::T + 16 * wv + j;
+    const float sgn = scale < 0.f ? -1.f : 1.f;
+    const bool single_tile = Cout <= 64;
+    if (single_tile) {
+        load_weights(0);
+        stage_bias(0);
+    }
+    __syncthreads();
 
-    for (int ct = 0; ct < Cout; ct += 64) {
-        if (ct > 0) {
-            __syncthreads();  // every wave is done with the previous tile's biases
-            stage_bias(ct);
-            load_weights(ct);
-            __syncthreads();
-        }
-
-        f32x4 best[4];
+    for (int ph = p0; ph < p1; ++ph) {
+        // issue the loads of the PK rows that pooled row ph + 1 adds
+        constexpr int NTOT = PK * NG;
+        constexpr int NPER = (NTOT + NT - 1) / NT;
+        uint4 pre[NPER][8];
+        const int nr0 = PK * (ph + 1) - pad + 2;
+        const bool more = ph + 1 < p1;
+        if (more) {
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) best[nt] = (f32x4){-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-
-#pragma unroll 1
-        for (int dy = 0; dy < PK; ++dy) {
-            const uint4 *tr = tile + dy * G::RS;
-#pragma unroll
-            for (int dx = 0; dx < PK; ++dx) {
-                f32x4 acc[4];
-#pragma unroll
-                for (int nt = 0; nt < 4; ++nt) acc[nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int s = 0; s < 3; ++s) {
-                    const uint4 bv = tr[off[s][dx]];
-                    const bf16x8 b = __builtin_bit_cast(bf16x8, bv);
-#pragma unroll
-                    for (int nt = 0; nt < 4; ++nt)
-                        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[nt][s], b, acc[nt], 0, 0, 0);
-                }
-#pragma unroll
-                for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) best[nt][r] = fmaxf(best[nt][r], sgn * acc[nt][r]);
+            for (int i = 0; i < NPER; ++i) {
+                const int e = threadIdx.x + i * NT;
+                if (e < NTOT) load_group(nr0 + e / NG, e % NG, pre[i]);
             }
         }
 
-        if (pw < PW) {
+        const int rbase = PK * ph - pad;
+        for (int ct = 0; ct < Cout; ct += 64) {
+            if (!single_tile) {
+                __syncthreads();
+                load_weights(ct);
+                stage_bias(ct);
+                __syncthreads();
+            }
+            f32x4 best[4];
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt)
+            for (int nt = 0; nt < 4; ++nt) best[nt] = (f32x4){-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll 1
+            for (int dy = 0; dy < PK; ++dy) {
+                const uint4 *rows[3];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int cl = 16 * nt + 4 * g4 + r;
-                    const int co = ct + cl;
-                    if (co < Cout) {
-                        const float v = sgn * best[nt][r] + s_bias[0][cl];
-                        y[(((size_t)n * Cout + co) * PH + ph) * PW + pw] =
-                            f32_to_bf16_rne(tanhf(v) * scale + s_bias[1][cl]);
+                for (int s = 0; s < 3; ++s) rows[s] = ring + ((rbase + dy + khs[s] + 4 * RING) % RING) * G::RS;
+#pragma unroll
+                for (int dx = 0; dx < PK; ++dx) {
+                    f32x4 acc[4];
+#pragma unroll
+                    for (int nt = 0; nt < 4; ++nt) acc[nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s = 0; s < 3; ++s) {
+                        const bf16x8 b = __builtin_bit_cast(bf16x8, rows[s][coff[s][dx]]);
+#pragma unroll
+                        for (int nt = 0; nt < 4; ++nt)
+                            acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[nt][s], b, acc[nt], 0, 0, 0);
                     }
+#pragma unroll
+                    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) best[nt][r] = fmaxf(best[nt][r], sgn * acc[nt][r]);
                 }
+            }
+            if (pw < PW) {
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int cl = 16 * nt + 4 * g4 + r;
+                        const int co = ct + cl;
+                        if (co < Cout) {
+                            const float v = sgn * best[nt][r] + s_bias[0][cl];
+                            y[(((size_t)n * Cout + co) * PH + ph) * PW + pw] =
+                                f32_to_bf16_rne(tanhf(v) * scale + s_bias[1][cl]);
+                        }
+                    }
+            }
         }
+
+        if (more) {
+#pragma unroll
+            for (int i = 0; i < NPER; ++i) {
+                const int e = threadIdx.x + i * NT;
+                if (e < NTOT) store_group(nr0 + e / NG, e % NG, pre[i]);
+            }
+        }
+        __syncthreads();
     }
 }
 
@@ -428,14 +470,36 @@ int launch_pk_npw(const void *x, const void *w, const float *cb, const float *b2
                   int dtype, int N, int Cin, int H, int W, int Cout, int pad, float scale, int PH,
                   int PW, hipStream_t stream) {
     const int npwt = (PW + 16 * NPW - 1) / (16 * NPW);
+    if (dtype == PS_BF16) {
+        // persistent: about two workgroups per CU, each a run of pooled rows
+        int dev = 0, ncu = 0;
+        if (hipGetDevice(&dev) != hipSuccess) return PS_ERR_HIP;
+        if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return PS_ERR_HIP;
+        const int64_t strips = (int64_t)N * npwt;
+        int64_t nseg = (2 * (int64_t)ncu + strips - 1) / strips;
+        if (nseg > PH) nseg = PH;
+        if (nseg < 1) nseg = 1;
+        const uint64_t nblocks = (uint64_t)strips * nseg;
+        if (nblocks > 0x7fffffffull) return PS_ERR_UNSUPPORTED;
+        // every strip starts at a multiple of 16*NPW*PK columns, so alignment is uniform
+        const bool vec = (pad % 8 == 0) && (W % 8 == 0);
+        if (vec)
+            hipLaunchKernelGGL((conv_pool_bf16<PK, NPW, true>), dim3((unsigned)nblocks),
+                               dim3(64 * NPW), 0, stream, (const uint16_t *)x, (const uint16_t *)w,
+                               cb, b2, (uint16_t *)y, Cin, H, W, Cout, pad, PH, PW, scale, npwt,
+                               (int)nseg);
+        else
+            hipLaunchKernelGGL((conv_pool_bf16<PK, NPW, false>), dim3((unsigned)nblocks),
+                               dim3(64 * NPW), 0, stream, (const uint16_t *)x, (const uint16_t *)w,
+                               cb, b2, (uint16_t *)y, Cin, H, W, Cout, pad, PH, PW, scale, npwt,
+                               (int)nseg);
+        return hipGetLastError() == hipSuccess ? PS_OK : PS_ERR_HIP;
+    }
     const uint64_t nblocks = (uint64_t)N * PH * npwt;
     if (nblocks > 0x7fffffffull) return PS_ERR_UNSUPPORTED;
     const dim3 grid((unsigned)nblocks), block(64 * NPW);
-    if (dtype == PS_BF16) {
-        hipLaunchKernelGGL((conv_pool_bf16<PK, NPW>), grid, block, 0, stream,
-                           (const uint16_t *)x, (const uint16_t *)w, cb, b2, (uint16_t *)y, Cin, H,
-                           W, Cout, pad, PH, PW, scale, npwt);
-    } else if (Cin <= 4) {
+    if (Cin <= 4) {
         hipLaunchKernelGGL((conv_pool_f32<PK, NPW, 1>), grid, block, 0, stream, (const float *)x,
                            (const float *)w, cb, b2, (float *)y, Cin, H, W, Cout, pad, PH, PW,
                            scale, npwt);
