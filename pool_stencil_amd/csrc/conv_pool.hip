@@ -65,7 +65,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     return (uint16_t)(u >> 16);
 }
 
-__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+// tanh from the identity tanh(v) = 1 - 2 / (exp(2v) + 1), with the hardware
+// exponential and reciprocal.  Absolute error is about 1e-7 over the whole
+// range (exp overflow gives +1, underflow -1); used where the result is
+// rounded to bf16 (one bf16 ulp near 1 is 2^-8).
+__device__ __forceinline__ float tanh_exp(float v) {
+    const float e = __expf(2.f * v);
+    return 1.f - 2.f * __builtin_amdgcn_rcpf(e + 1.f);
+}
 
 // ---------------------------------------------------------------- fp32 ---
 #ifndef PS_CONV_MIN_WAVES
@@ -303,20 +310,23 @@ __global__ __launch_bounds__(64 * NPW, 2) void conv_pool_bf16(
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const int c = 8 * u + k;
-            uint32_t h[8];
+            // column k sits in word k/2 of each channel's vector, low half for even k;
+            // one byte permute packs that half of two channels into one word
+            const uint32_t sel = (k & 1) ? 0x07060302u : 0x05040100u;
+            uint32_t wd[8];
 #pragma unroll
-            for (int ci = 0; ci < 8; ++ci) {
-                const uint32_t wd = (k >> 1) == 0 ? v[ci].x : (k >> 1) == 1 ? v[ci].y
-                                  : (k >> 1) == 2 ? v[ci].z : v[ci].w;
-                h[ci] = (k & 1) ? (wd >> 16) : (wd & 0xffffu);
-            }
+            for (int ci = 0; ci < 8; ++ci)
+                wd[ci] = (k >> 1) == 0 ? v[ci].x : (k >> 1) == 1 ? v[ci].y
+                       : (k >> 1) == 2 ? v[ci].z : v[ci].w;
             if (c < G::COLS)
-                rrow[(c % PK) * G::Q + c / PK] = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16),
-                                                           h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+                rrow[(c % PK) * G::Q + c / PK] =
+                    make_uint4(__builtin_amdgcn_perm(wd[1], wd[0], sel), __builtin_amdgcn_perm(wd[3], wd[2], sel),
+                               __builtin_amdgcn_perm(wd[5], wd[4], sel), __builtin_amdgcn_perm(wd[7], wd[6], sel));
         }
     };
 
     // A operands: lane holds w[co = ct + 16*nt + j][ci = 0..7][tap = 4*s + g4]
+    const uint32_t wsign = scale < 0.f ? 0x80008000u : 0u;
     bf16x8 wa[4][3];
     auto load_weights = [&](int ct) {
 #pragma unroll
@@ -332,11 +342,13 @@ __global__ __launch_bounds__(64 * NPW, 2) void conv_pool_bf16(
                     const uint32_t v = w[ok ? ((size_t)co * Cin + ci) * 9 + tap : 0];
                     hv[ci] = ok ? v : 0u;
                 }
+                // negative scale: negate the weights (exact), so the window max of the
+                // negated sums is minus the window min of the sums
                 uint4 pk;
-                pk.x = hv[0] | (hv[1] << 16);
-                pk.y = hv[2] | (hv[3] << 16);
-                pk.z = hv[4] | (hv[5] << 16);
-                pk.w = hv[6] | (hv[7] << 16);
+                pk.x = (hv[0] | (hv[1] << 16)) ^ wsign;
+                pk.y = (hv[2] | (hv[3] << 16)) ^ wsign;
+                pk.z = (hv[4] | (hv[5] << 16)) ^ wsign;
+                pk.w = (hv[6] | (hv[7] << 16)) ^ wsign;
                 wa[nt][s] = __builtin_bit_cast(bf16x8, pk);
             }
         }
@@ -435,20 +447,22 @@ __global__ __launch_bounds__(64 * NPW, 2) void conv_pool_bf16(
 #pragma unroll
                     for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) best[nt][r] = fmaxf(best[nt][r], sgn * acc[nt][r]);
+                        for (int r = 0; r < 4; ++r) best[nt][r] = fmaxf(best[nt][r], acc[nt][r]);
                 }
             }
             if (pw < PW) {
+                // output (n, co, ph, pw): the lane's first channel, then constant strides
+                const size_t cplane = (size_t)PH * PW;
+                uint16_t *yrow = y + ((size_t)n * Cout + ct + 4 * g4) * cplane + (size_t)ph * PW + pw;
 #pragma unroll
                 for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int cl = 16 * nt + 4 * g4 + r;
-                        const int co = ct + cl;
-                        if (co < Cout) {
+                        if (ct + cl < Cout) {
                             const float v = sgn * best[nt][r] + s_bias[0][cl];
-                            y[(((size_t)n * Cout + co) * PH + ph) * PW + pw] =
-                                f32_to_bf16_rne(tanhf(v) * scale + s_bias[1][cl]);
+                            yrow[(size_t)(16 * nt + r) * cplane] =
+                                f32_to_bf16_rne(tanh_exp(v) * scale + s_bias[1][cl]);
                         }
                     }
             }
