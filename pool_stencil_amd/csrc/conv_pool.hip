@@ -75,12 +75,24 @@ __device__ __forceinline__ float tanh_exp(float v) {
 }
 
 // ---------------------------------------------------------------- fp32 ---
+// fp32 conv tuning: 16-byte halo loads issued per batch (bounds the registers the
+// fill holds next to the resident weights), window columns per unrolled group (0 =
+// all), and the minimum resident waves per SIMD asked of the register allocator
+// for pool windows up to 4 (three 52 KB workgroups then share a CU's LDS).  On
+// MI355X, batches of 7 with 3 waves/SIMD took the 8->64 k3 + pool-4 workload from
+// 0.745 to 0.68 ms.
+#ifndef PS_CONV_FILL_BATCH
+#define PS_CONV_FILL_BATCH 7
+#endif
+#ifndef PS_CONV_DXG
+#define PS_CONV_DXG 0
+#endif
 #ifndef PS_CONV_MIN_WAVES
-#define PS_CONV_MIN_WAVES 1
+#define PS_CONV_MIN_WAVES 3
 #endif
 
 template <int PK, int NPW, int CING>
-__global__ __launch_bounds__(64 * NPW, PS_CONV_MIN_WAVES) void conv_pool_f32(
+__global__ __launch_bounds__(64 * NPW, (PK <= 4 ? PS_CONV_MIN_WAVES : 1)) void conv_pool_f32(
     const float *__restrict__ x, const float *__restrict__ w, const float *__restrict__ cb,
     const float *__restrict__ b2, float *__restrict__ y, int Cin, int H, int W, int Cout,
     int pad, int PH, int PW, float scale, int npwt) {
@@ -143,42 +155,47 @@ __global__ __launch_bounds__(64 * NPW, PS_CONV_MIN_WAVES) void conv_pool_f32(
         constexpr int TOTAL = CINP * G::ROWS * NV;
         constexpr int PER = (TOTAL + NT - 1) / NT;
         const bool vec = ((ic0 & 3) == 0) && ((W & 3) == 0);
-        float4 buf[PER];
+        // loads are issued FB vectors at a time (all of them when FB >= PER)
+        constexpr int FB = PS_CONV_FILL_BATCH > 0 && PS_CONV_FILL_BATCH < PER ? PS_CONV_FILL_BATCH : PER;
 #pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int e = threadIdx.x + i * NT;
-            const int u = e % NV;
-            const int row = e / NV;
-            const int r = row % G::ROWS;
-            const int ci = row / G::ROWS;
-            const int ir = ir0 + r, ic = ic0 + 4 * u;
-            const bool rok = e < TOTAL && ci < Cin && ir >= 0 && ir < H;
-            const float *src = xn + ((size_t)ci * H + ir) * W + ic;
-            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (vec) {
-                if (rok && ic >= 0 && ic < W) v = *(const float4 *)src;
-            } else if (rok) {
-                if (ic >= 0 && ic < W) v.x = src[0];
-                if (ic + 1 >= 0 && ic + 1 < W) v.y = src[1];
-                if (ic + 2 >= 0 && ic + 2 < W) v.z = src[2];
-                if (ic + 3 >= 0 && ic + 3 < W) v.w = src[3];
-            }
-            buf[i] = v;
-        }
+        for (int i0 = 0; i0 < PER; i0 += FB) {
+            float4 buf[FB];
 #pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int e = threadIdx.x + i * NT;
-            if (e < TOTAL) {
+            for (int ii = 0; ii < FB; ++ii) {
+                const int e = threadIdx.x + (i0 + ii) * NT;
                 const int u = e % NV;
                 const int row = e / NV;
                 const int r = row % G::ROWS;
                 const int ci = row / G::ROWS;
-                float *trow = tile + ci * PS + r * G::RS;
-                const float vv[4] = {buf[i].x, buf[i].y, buf[i].z, buf[i].w};
+                const int ir = ir0 + r, ic = ic0 + 4 * u;
+                const bool rok = i0 + ii < PER && e < TOTAL && ci < Cin && ir >= 0 && ir < H;
+                const float *src = xn + ((size_t)ci * H + ir) * W + ic;
+                float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (vec) {
+                    if (rok && ic >= 0 && ic < W) v = *(const float4 *)src;
+                } else if (rok) {
+                    if (ic >= 0 && ic < W) v.x = src[0];
+                    if (ic + 1 >= 0 && ic + 1 < W) v.y = src[1];
+                    if (ic + 2 >= 0 && ic + 2 < W) v.z = src[2];
+                    if (ic + 3 >= 0 && ic + 3 < W) v.w = src[3];
+                }
+                buf[ii] = v;
+            }
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const int c = 4 * u + k;
-                    if (c < G::COLS) trow[(c % PK) * G::Q + c / PK] = vv[k];
+            for (int ii = 0; ii < FB; ++ii) {
+                const int e = threadIdx.x + (i0 + ii) * NT;
+                if (i0 + ii < PER && e < TOTAL) {
+                    const int u = e % NV;
+                    const int row = e / NV;
+                    const int r = row % G::ROWS;
+                    const int ci = row / G::ROWS;
+                    float *trow = tile + ci * PS + r * G::RS;
+                    const float vv[4] = {buf[ii].x, buf[ii].y, buf[ii].z, buf[ii].w};
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const int c = 4 * u + k;
+                        if (c < G::COLS) trow[(c % PK) * G::Q + c / PK] = vv[k];
+                    }
                 }
             }
         }
@@ -203,8 +220,14 @@ __global__ __launch_bounds__(64 * NPW, PS_CONV_MIN_WAVES) void conv_pool_f32(
 #pragma unroll 1
         for (int dy = 0; dy < PK; ++dy) {
             const float *tr = tb + dy * G::RS;
+            // window columns in groups of DXG: fewer live accumulators when DXG < PK
+            constexpr int DXG = PS_CONV_DXG > 0 && PS_CONV_DXG < PK ? PS_CONV_DXG : PK;
+#pragma unroll 1
+            for (int dx0 = 0; dx0 < PK; dx0 += DXG)
 #pragma unroll
-            for (int dx = 0; dx < PK; ++dx) {
+            for (int dk = 0; dk < DXG; ++dk) {
+                const int dx = dx0 + dk;
+                if (DXG < PK && dx >= PK) break;
                 f32x4 acc[4];
 #pragma unroll
                 for (int nt = 0; nt < 4; ++nt) acc[nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
@@ -254,7 +277,7 @@ __global__ __launch_bounds__(64 * NPW, PS_CONV_MIN_WAVES) void conv_pool_f32(
 // rows that pooled row ph+1 adds are loaded from HBM into registers during the
 // MFMA work of row ph and written to the ring afterwards.  One barrier per row.
 template <int PK, int NPW, bool VEC>
-__global__ __launch_bounds__(64 * NPW, 2) void conv_pool_bf16(
+__global__ __launch_bounds__(64 * NPW, (PK <= 4 ? 2 : 1)) void conv_pool_bf16(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, const float *__restrict__ cb,
     const float *__restrict__ b2, uint16_t *__restrict__ y, int Cin, int H, int W, int Cout,
     int pad, int PH, int PW, float scale, int npwt, int nseg) {
