@@ -45,10 +45,10 @@ CONVT_BYTES = 128 * 64 * 64 * 64 * 4 + 128 * 128 * 129 * 129 * 4 + 64 * 128 * 16
 # x1.0.  `src` is the hash of the kernel's sources when the counters were taken; a
 # kernel edited since then reports traffic null.  See profiles/traffic_*.md.
 TRAFFIC = {
-    "conv": {"src": "f836461b7418e386", "fetch_bytes": 266806354, "write_bytes": 130668896},
-    "maxpool": {"src": "231157ba21664983", "fetch_bytes": 2336400059, "write_bytes": 2140966016},
-    "convT": {"src": "4756821d0a67bf5e", "fetch_bytes": 756348644, "write_bytes": 2830417056},
-    "conv_bf16": {"src": "f836461b7418e386", "fetch_bytes": 136834562, "write_bytes": 82845024},
+    "conv": {"src": "dc51f5a7b7f8394b", "fetch_bytes": 266847985, "write_bytes": 130658688},
+    "maxpool": {"src": "231157ba21664983", "fetch_bytes": 2336400337, "write_bytes": 2140942016},
+    "convT": {"src": "4756821d0a67bf5e", "fetch_bytes": 757553201, "write_bytes": 2829604224},
+    "conv_bf16": {"src": "dc51f5a7b7f8394b", "fetch_bytes": 136757779, "write_bytes": 83146208},
 }
 KERNEL_SOURCES = {
     "conv": ["conv_pool.hip", "ps_internal.h"],
