@@ -10,6 +10,9 @@ synthetic workload, on inputs already resident in HBM:
   convT       x fp32 [128,64,64,64] -> convT 64->128 k4 s2 p1 op1 + softmax + bias + *2
               + sigmoid -> [128,128,129,129]   (136.37 GFLOP over the valid taps)
   conv_bf16   the conv workload with bf16 x, w and output (74.91 GFLOP)
+  conv_general x fp32 [32,64,128,128] -> conv 64->128 k3 p1 + tanh + *2 + bias
+              + maxpool k3 s2 p1 (overlapping windows) -> [32,128,64,64]
+              (77.31 GFLOP: every 128x128 conv output is read by some window)
 
 `value` is the fused conv+maxpool throughput (GFLOP/s, fp32) -- the first
 figure of the headline metric; the max-pool's GB/s (the second figure) and the
@@ -36,6 +39,7 @@ PEAK_HBM = 8.0e12         # MI355X HBM3E, B/s
 CONV_FLOP = 2 * 72 * 128 * 64 * 252 * 252
 CONV_FLOP_PAGE = 2 * 72 * 128 * 64 * 254 * 254     # the page's count over all 254x254 outputs
 POOL_BYTES = 32 * 64 * 512 * 512 * 4 + 32 * 64 * 511 * 511 * 4
+CONV_GENERAL_FLOP = 2 * 64 * 9 * 32 * 128 * 128 * 128
 CONVT_FLOP = 2 * 128 * 64 * 128 * 255 * 255
 CONVT_BYTES = 128 * 64 * 64 * 64 * 4 + 128 * 128 * 129 * 129 * 4 + 64 * 128 * 16 * 4
 
@@ -55,6 +59,7 @@ KERNEL_SOURCES = {
     "conv_bf16": ["conv_pool.hip", "ps_internal.h"],
     "maxpool": ["maxpool.hip", "ps_internal.h"],
     "convT": ["convt_softmax.hip", "ps_internal.h"],
+    "conv_general": ["conv_general.hip", "ps_internal.h"],
 }
 
 
@@ -81,7 +86,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (profiling runs)")
-    ap.add_argument("--ops", default="conv,maxpool,convT,conv_bf16")
+    ap.add_argument("--ops", default="conv,maxpool,convT,conv_bf16,conv_general")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a 2 GiB device-to-device copy instead (counter calibration)")
     return ap.parse_args()
@@ -167,6 +172,13 @@ def main():
         runs["conv_bf16"] = lambda xb=xb, wb=wb, cbb=cbb, b2b=b2b, outb=outb: (
             ps.conv_tanh_scale_bias_maxpool(xb, wb, cbb, b2b, 2.0, 4, out=outb))
         del c
+    if "conv_general" in ops:
+        c = inputgen.workload("conv_general")
+        xg, wg, cbg, b2g = put(c["x"]), put(c["w"]), put(c["conv_bias"]), put(c["bias2"])
+        outg = torch.empty((32, 128, 64, 64), dtype=torch.float32, device=dev)
+        runs["conv_general"] = lambda xg=xg, wg=wg, cbg=cbg, b2g=b2g, outg=outg: (
+            ps.conv_tanh_scale_bias_maxpool(xg, wg, cbg, b2g, 2.0, 3, 2, 1, 1, 1, 1, 1, out=outg))
+        del c
     torch.cuda.synchronize()
     print(f"[bench] inputs ready in {time.time() - t0:.1f}s; ops {list(runs)}",
           file=sys.stderr, flush=True)
@@ -239,6 +251,16 @@ def main():
                          "unit": "TFLOP/s", "frac": ach / PEAK_BF16, "traffic": traffic("conv_bf16"),
                          "frac_of_fp32_peak": ach / PEAK_FP32}}
 
+    if "conv_general" in runs:
+        mean, med, mn = stats("conv_general")
+        ach = CONV_GENERAL_FLOP / (mean * 1e-3)
+        out_ops["conv_general"] = {
+            "value": ach / 1e9, "unit": "GFLOP/s", "ms_mean": mean, "ms_median": med, "ms_min": mn,
+            "gflop_per_launch": CONV_GENERAL_FLOP / 1e9,
+            "roofline": {"bound": "mfma", "achieved": ach / 1e12, "peak": PEAK_FP32 / 1e12,
+                         "unit": "TFLOP/s", "frac": ach / PEAK_FP32,
+                         "traffic": traffic("conv_general")}}
+
     head = "conv" if "conv" in out_ops else next(iter(out_ops))
     cpu = None
     if not args.no_cpu_baseline and head == "conv":
@@ -265,6 +287,8 @@ def main():
             "convT_workload": "convT 64->128 k4 s2 p1 op1 + softmax(c) + bias + *2 + sigmoid, "
                               "x fp32 [128,64,64,64] -> [128,128,129,129]",
             "conv_bf16_workload": "conv workload with bf16 x/w/out, fp32 accumulate",
+            "conv_general_workload": "conv2d 64->128 k3 p1 + tanh + *2 + bias + maxpool k3 s2 p1, "
+                                     "x fp32 [32,64,128,128] -> [32,128,64,64]",
         },
         "roofline": out_ops[head]["roofline"],
         "cpu_baseline": cpu,

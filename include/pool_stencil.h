@@ -1,10 +1,11 @@
 /*
  * pool_stencil -- fused sliding-window stencils for AMD Instinct MI355X (gfx950).
  *
- * C ABI of libpool_stencil.so.  Three operations:
+ * C ABI of libpool_stencil.so.  Operations:
  *
  *   ps_conv_tanh_scale_bias_maxpool     Conv2d -> tanh -> *scale -> +bias2[c] -> MaxPool2d,
  *                                       fused: the conv output never reaches memory
+ *   ps_conv2d                           Conv2d + bias (the unfused pipeline's first stage)
  *   ps_maxpool2d                        MaxPool2d (stride-1 overlapping windows included)
  *   ps_convT_softmax_bias_scale_sigmoid ConvTranspose2d -> softmax over channels
  *                                       -> +bias2[c] -> *scale -> sigmoid, fused
@@ -96,15 +97,36 @@ int ps_convT2d_out_dim(int in, int k, int stride, int pad, int output_padding, i
  * conv_bias [Cout] float32, or NULL for a conv without bias
  * bias2     [Cout] float32 (the [C,1,1] bias parameter after the conv)
  * y         [N,Cout,PH,PW]    dtype; bf16 output is rounded to nearest even
- * pool_stride <= 0 means pool_stride = pool_k.
- * Supported (else PS_ERR_UNSUPPORTED): kH = kW = 3, conv_stride = 1, conv_dil = 1,
- * 0 <= conv_pad <= 2, 1 <= Cin <= 64, pool_stride = pool_k, 2 <= pool_k <= 8,
- * pool_pad = 0, pool_dil = 1. */
+ * pool_stride <= 0 means pool_stride = pool_k.  A pool window lying wholly in
+ * the pool's padding gives -inf (the plain definition's max over -inf values).
+ * Any conv kernel size, stride, padding and dilation, any Cin and Cout, and any
+ * pool window / stride / padding / dilation are accepted, with two limits of
+ * the tiling: the pool window's extent (pool_k-1)*pool_dil+1 must be <= 16, and
+ * the conv input patch of one pooled output plus 64 x 4 x kH*kW weights must fit
+ * the 160 KB of LDS of a compute unit (kH*kW <= 144 always does).  Beyond them
+ * the call returns PS_ERR_UNSUPPORTED.  The 3x3, stride-1, dilation-1,
+ * conv_pad <= 2, Cin <= 8, disjoint-window (pool_stride = pool_k <= 8, no pool
+ * padding or dilation) case runs a kernel of its own with the weights held in
+ * registers; every other case runs the general tiled kernel. */
 int ps_conv_tanh_scale_bias_maxpool(
     const void *x, const void *w, const float *conv_bias, const float *bias2, void *y,
     int dtype, int N, int Cin, int H, int W, int Cout, int kH, int kW, int conv_stride,
     int conv_pad, int conv_dil, float scale, int pool_k, int pool_stride, int pool_pad,
     int pool_dil, void *stream);
+
+/* ------------------------------------------------------------ conv 2d --- */
+/* The first stage of the l2_p82 page's unfused pipeline (its first kernel
+ * writes the full conv output, a second kernel applies the epilogue and the
+ * pool); also a plain nn.Conv2d forward:
+ *   y[n,co,oh,ow] = bias[co] + sum_{ci,kh,kw} x[n,ci,oh*s-p+kh*d, ow*s-p+kw*d] * w[co,ci,kh,kw]
+ * (cross-correlation, zero padding).
+ * x [N,Cin,H,W] dtype, w [Cout,Cin,kH,kW] dtype, bias [Cout] float32 or NULL,
+ * y [N,Cout,OH,OW] dtype (bf16: fp32 accumulation, output rounded to nearest even).
+ * Any kernel size, stride, padding, dilation and channel counts, within the
+ * same LDS limit as the fused call (kH*kW <= 144 always fits). */
+int ps_conv2d(const void *x, const void *w, const float *bias, void *y, int dtype, int N,
+              int Cin, int H, int W, int Cout, int kH, int kW, int stride, int pad, int dil,
+              void *stream);
 
 /* ---------------------------------------------------------- max-pool 2d --- */
 /* l1_p42 page (problem statement; PyTorch's implicit -inf padding):

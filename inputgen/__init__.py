@@ -105,7 +105,7 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 # ---------------------------------------------------------------------------
 # Workload table.  Index = position in the list of the five workloads.
 # ---------------------------------------------------------------------------
-WORKLOADS = ["tiny_conv", "maxpool", "conv", "convT", "conv_bf16"]
+WORKLOADS = ["tiny_conv", "maxpool", "conv", "convT", "conv_bf16", "conv_general"]
 
 
 def _conv_case(idx, N, Cin, H, W, Cout, wdist, b2dist, dtype="f32", N_take=None):
@@ -159,6 +159,13 @@ def workload(name: str) -> dict:
         return dict(op="convT", dtype="f32", x=x, w=w, convT_bias=cb, bias2=b2,
                     N=128, Cin=64, H=64, W=64, Cout=128, k=4, stride=2, pad=1,
                     output_padding=1, dil=1, scale=2.0)
+    if name == "conv_general":
+        # The fused op beyond the 3x3 / 8-channel / disjoint-window case: 64 -> 128
+        # channels, 3x3 conv with padding 1, overlapping 3x3 stride-2 pool with
+        # padding 1; value distributions as in the conv workload.
+        c = random_conv_case(seed_for(idx, 0), 32, 64, 128, 128, 128, conv_pad=1,
+                             pool_k=3, pool_stride=2, pool_pad=1)
+        return c
     raise KeyError(name)
 
 

@@ -9,6 +9,7 @@ importing this package fails if the library has not been built.
 
 Operations (same names as the C entry points, without the ps_ prefix):
     conv_tanh_scale_bias_maxpool(x, w, conv_bias, bias2, scale, pool_k, ...)
+    conv2d(x, w, bias=None, stride=1, pad=0, dil=1)
     maxpool2d(x, k, stride=None, pad=0, dil=1)
     convT_softmax_bias_scale_sigmoid(x, w, convT_bias, bias2, scale, ...)
 """
@@ -26,7 +27,7 @@ PS_F32, PS_BF16 = 0, 1
 # Every symbol include/pool_stencil.h declares.
 EXPORTS = (
     "ps_status_string", "ps_version", "ps_conv2d_out_dim", "ps_pool2d_out_dim",
-    "ps_convT2d_out_dim", "ps_conv_tanh_scale_bias_maxpool", "ps_maxpool2d",
+    "ps_convT2d_out_dim", "ps_conv_tanh_scale_bias_maxpool", "ps_conv2d", "ps_maxpool2d",
     "ps_convT_softmax_bias_scale_sigmoid",
 )
 
@@ -45,7 +46,7 @@ def _load() -> ctypes.CDLL:
     import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python -m pool_stencil_amd.build` "
+            f"{LIB_PATH} is missing: build it with `python pool_stencil_amd/build.py` "
             "(or __graft_entry__.build()) before using pool_stencil_amd")
     lib = ctypes.CDLL(LIB_PATH)
     i, f, p = ctypes.c_int, ctypes.c_float, ctypes.c_void_p
@@ -56,10 +57,11 @@ def _load() -> ctypes.CDLL:
     lib.ps_pool2d_out_dim.argtypes = [i, i, i, i, i, ctypes.POINTER(i)]
     lib.ps_convT2d_out_dim.argtypes = [i, i, i, i, i, i, ctypes.POINTER(i)]
     lib.ps_conv_tanh_scale_bias_maxpool.argtypes = [p, p, p, p, p] + [i] * 11 + [f] + [i] * 4 + [p]
+    lib.ps_conv2d.argtypes = [p, p, p, p] + [i] * 11 + [p]
     lib.ps_maxpool2d.argtypes = [p, p] + [i] * 8 + [p]
     lib.ps_convT_softmax_bias_scale_sigmoid.argtypes = [p, p, p, p, p] + [i] * 10 + [f, p]
     for name in ("ps_conv2d_out_dim", "ps_pool2d_out_dim", "ps_convT2d_out_dim",
-                 "ps_conv_tanh_scale_bias_maxpool", "ps_maxpool2d",
+                 "ps_conv_tanh_scale_bias_maxpool", "ps_conv2d", "ps_maxpool2d",
                  "ps_convT_softmax_bias_scale_sigmoid"):
         getattr(lib, name).restype = i
     return lib
@@ -171,6 +173,37 @@ def conv_tanh_scale_bias_maxpool(x, w, conv_bias, bias2, scale, pool_k, pool_str
         _stream(stream))
     if st != PS_OK:
         raise PsError(st, "ps_conv_tanh_scale_bias_maxpool")
+    return out
+
+
+def conv2d(x, w, bias=None, stride=1, pad=0, dil=1, out=None, stream=None):
+    """Conv2d + bias (cross-correlation, zero padding) of an NCHW tensor.
+
+    x [N,Cin,H,W] and w [Cout,Cin,kH,kW] share a dtype (float32 or bfloat16); bias
+    (optional) is float32 [Cout].  Returns [N,Cout,OH,OW] in x's dtype."""
+    torch = _torch()
+    _check(x, "x", (torch.float32, torch.bfloat16))
+    _check(w, "w", (x.dtype,), x.device)
+    _check(bias, "bias", (torch.float32,), x.device)
+    N, Cin, H, W = x.shape
+    Cout, Cin_w, kH, kW = w.shape
+    if Cin_w != Cin:
+        raise ValueError(f"w has {Cin_w} input channels, x has {Cin}")
+    if bias is not None and bias.numel() != Cout:
+        raise ValueError("bias must hold Cout elements")
+    OH = conv2d_out_dim(H, kH, stride, pad, dil)
+    OW = conv2d_out_dim(W, kW, stride, pad, dil)
+    if out is None:
+        out = torch.empty((N, Cout, OH, OW), dtype=x.dtype, device=x.device)
+    else:
+        _check(out, "out", (x.dtype,), x.device)
+        if tuple(out.shape) != (N, Cout, OH, OW):
+            raise ValueError(f"out has shape {tuple(out.shape)}, expected {(N, Cout, OH, OW)}")
+    dtype = PS_BF16 if x.dtype == torch.bfloat16 else PS_F32
+    st = _lib.ps_conv2d(_ptr(x), _ptr(w), _ptr(bias), _ptr(out), dtype, N, Cin, H, W, Cout,
+                        kH, kW, stride, pad, dil, _stream(stream))
+    if st != PS_OK:
+        raise PsError(st, "ps_conv2d")
     return out
 
 

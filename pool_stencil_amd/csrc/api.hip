@@ -119,14 +119,38 @@ int ps_conv_tanh_scale_bias_maxpool(const void *x, const void *w, const float *c
     if (st != PS_OK) return st;
     if (too_big(N, Cin, H, W) || too_big(N, Cout, PH, PW) || too_big(Cout, Cin, kH, kW))
         return PS_ERR_SHAPE;
-    if (kH != 3 || kW != 3 || conv_stride != 1 || conv_dil != 1 || conv_pad > 2)
-        return PS_ERR_UNSUPPORTED;
-    if (Cin > 8 || pool_stride != pool_k || pool_k < 2 || pool_k > 8 || pool_pad != 0 ||
-        pool_dil != 1)
-        return PS_ERR_UNSUPPORTED;
     if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return PS_ERR_ALIGN;
-    return ps::launch_conv_pool(x, w, conv_bias, bias2, y, dtype, N, Cin, H, W, Cout, conv_pad,
-                                OH, OW, scale, pool_k, PH, PW, (hipStream_t)stream);
+    // The 3x3 / stride-1 / few-channel / disjoint-window case has its own kernel with
+    // the weights resident in registers; everything else takes the general kernel.
+    const bool small_k3 = kH == 3 && kW == 3 && conv_stride == 1 && conv_dil == 1 &&
+                          conv_pad <= 2 && Cin <= 8 && pool_stride == pool_k && pool_k >= 2 &&
+                          pool_k <= 8 && pool_pad == 0 && pool_dil == 1;
+    if (small_k3)
+        return ps::launch_conv_pool(x, w, conv_bias, bias2, y, dtype, N, Cin, H, W, Cout,
+                                    conv_pad, OH, OW, scale, pool_k, PH, PW, (hipStream_t)stream);
+    return ps::launch_conv_general(x, w, conv_bias, bias2, y, dtype, 0, N, Cin, H, W, Cout, kH,
+                                   kW, conv_stride, conv_pad, conv_dil, OH, OW, scale, pool_k,
+                                   pool_stride, pool_pad, pool_dil, PH, PW, (hipStream_t)stream);
+}
+
+int ps_conv2d(const void *x, const void *w, const float *bias, void *y, int dtype, int N,
+              int Cin, int H, int W, int Cout, int kH, int kW, int stride, int pad, int dil,
+              void *stream) {
+    if (!x || !w || !y) return PS_ERR_NULL;
+    if (dtype != PS_F32 && dtype != PS_BF16) return PS_ERR_PARAM;
+    if (N < 1 || Cin < 1 || H < 1 || W < 1 || Cout < 1) return PS_ERR_SHAPE;
+    if (kH < 1 || kW < 1 || stride < 1 || dil < 1 || pad < 0) return PS_ERR_PARAM;
+    int OH, OW;
+    int st = ps_conv2d_out_dim(H, kH, stride, pad, dil, &OH);
+    if (st != PS_OK) return st;
+    st = ps_conv2d_out_dim(W, kW, stride, pad, dil, &OW);
+    if (st != PS_OK) return st;
+    if (too_big(N, Cin, H, W) || too_big(N, Cout, OH, OW) || too_big(Cout, Cin, kH, kW))
+        return PS_ERR_SHAPE;
+    if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return PS_ERR_ALIGN;
+    return ps::launch_conv_general(x, w, bias, nullptr, y, dtype, 1, N, Cin, H, W, Cout, kH, kW,
+                                   stride, pad, dil, OH, OW, 1.f, 1, 1, 0, 1, OH, OW,
+                                   (hipStream_t)stream);
 }
 
 int ps_convT_softmax_bias_scale_sigmoid(const float *x, const float *w, const float *convT_bias,

@@ -58,13 +58,6 @@ struct TileGeom {
     static constexpr int RS = PK * Q;        // entries per tile row
 };
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);  // NaN stays NaN
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-}
-
 // tanh from the identity tanh(v) = 1 - 2 / (exp(2v) + 1), with the hardware
 // exponential and reciprocal.  Absolute error is about 1e-7 over the whole
 // range (exp overflow gives +1, underflow -1); used where the result is

@@ -19,9 +19,30 @@ int launch_conv_pool(const void *x, const void *w, const float *conv_bias, const
                      int OH, int OW, float scale, int pool_k, int PH, int PW,
                      hipStream_t stream);
 
+// General fused conv + pool (epi = 0) or plain conv + bias (epi = 1; pool
+// arguments ignored, output [N,Cout,OH,OW]).  Any kernel size, stride,
+// padding, dilation and channel counts; returns PS_ERR_UNSUPPORTED (before any
+// HIP call) when no tile of the kernel fits the arguments.
+int launch_conv_general(const void *x, const void *w, const float *conv_bias, const float *bias2,
+                        void *y, int dtype, int epi, int N, int Cin, int H, int W, int Cout,
+                        int kH, int kW, int cs, int cp, int cd, int OH, int OW, float scale,
+                        int pk, int ps, int pp, int pd, int PH, int PW, hipStream_t stream);
+
 int launch_convT_softmax(const float *x, const float *w, const float *convT_bias,
                          const float *bias2, float *y, int N, int Cin, int H, int W, int Cout,
                          int OH, int OW, float scale, hipStream_t stream);
+
+// fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float((uint32_t)b << 16);
+}
 
 // Blocks of one launch are handed to the 8 XCDs of an MI355X round-robin
 // (block b runs on XCD b % 8).  This remaps the hardware block index so that

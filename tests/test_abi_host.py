@@ -17,8 +17,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def ps():
     lib_path = os.path.join(ROOT, "pool_stencil_amd", "libpool_stencil.so")
     if not os.path.exists(lib_path):
-        from pool_stencil_amd import build as b
-        b.build()
+        import __graft_entry__
+        __graft_entry__.build()
     import pool_stencil_amd
     return pool_stencil_amd
 
@@ -99,13 +99,36 @@ def test_conv_pool_validation(ps):
     assert _conv(lib, H=2) == ps.PS_ERR_SHAPE            # conv window does not fit
     assert _conv(lib, H=5) == ps.PS_ERR_SHAPE            # conv 3 rows < pool 4
     assert _conv(lib, cp=-1) == ps.PS_ERR_PARAM
-    assert _conv(lib, kH=5, kW=5) == ps.PS_ERR_UNSUPPORTED
-    assert _conv(lib, cs=2) == ps.PS_ERR_UNSUPPORTED
-    assert _conv(lib, Cin=9) == ps.PS_ERR_UNSUPPORTED
-    assert _conv(lib, pst=2) == ps.PS_ERR_UNSUPPORTED     # overlapping pool windows
-    assert _conv(lib, pk=9) == ps.PS_ERR_UNSUPPORTED
+    # Every other argument combination is covered by one of the two kernels; only a
+    # pool window wider than 16 conv outputs and a conv kernel whose weights do not
+    # fit the LDS of a compute unit remain unsupported.  (Supported combinations are
+    # not exercised here: with the fake pointers they would launch a kernel.)
+    assert _conv(lib, pk=17, H=40, W=40) == ps.PS_ERR_UNSUPPORTED
+    assert _conv(lib, pk=9, pd=2, H=40, W=40) == ps.PS_ERR_UNSUPPORTED
+    assert _conv(lib, kH=13, kW=13, pk=2, H=64, W=64) == ps.PS_ERR_UNSUPPORTED
     assert _conv(lib, x=MISALIGNED) == ps.PS_ERR_ALIGN
     assert _conv(lib, y=MISALIGNED) == ps.PS_ERR_ALIGN
+    assert _conv(lib, kH=5, kW=5, y=MISALIGNED) == ps.PS_ERR_ALIGN
+
+
+def _conv2d(lib, x=FAKE, w=FAKE, b=None, y=FAKE, dtype=0, N=1, Cin=8, H=16, W=16, Cout=16,
+            kH=3, kW=3, s=1, p=0, d=1):
+    return lib.ps_conv2d(x, w, b, y, dtype, N, Cin, H, W, Cout, kH, kW, s, p, d, None)
+
+
+def test_conv2d_validation(ps):
+    lib = ps.lib()
+    assert _conv2d(lib, x=None) == ps.PS_ERR_NULL
+    assert _conv2d(lib, y=None) == ps.PS_ERR_NULL
+    assert _conv2d(lib, dtype=2) == ps.PS_ERR_PARAM
+    assert _conv2d(lib, Cout=0) == ps.PS_ERR_SHAPE
+    assert _conv2d(lib, H=2) == ps.PS_ERR_SHAPE
+    assert _conv2d(lib, s=0) == ps.PS_ERR_PARAM
+    assert _conv2d(lib, p=-1) == ps.PS_ERR_PARAM
+    assert _conv2d(lib, d=0) == ps.PS_ERR_PARAM
+    assert _conv2d(lib, w=MISALIGNED) == ps.PS_ERR_ALIGN
+    assert _conv2d(lib, kH=13, kW=13, H=32, W=32) == ps.PS_ERR_UNSUPPORTED
+    assert _conv2d(lib, N=1 << 20, Cin=1 << 20) == ps.PS_ERR_SHAPE
 
 
 def _pool(lib, x=FAKE, y=FAKE, N=1, C=1, H=8, W=8, k=4, s=1, p=1, d=1):
