@@ -25,9 +25,9 @@
 //   - patch: [ci][row][col], channel stride padded to 16 (mod 64) words, so
 //     the four lane groups of a wave (one input channel each) use disjoint
 //     banks;
-//   - weights: [tap][ci][co], the co position XOR-swizzled by (ci mod 4) in
-//     16-channel blocks, so the four lane groups read four different
-//     16-bank blocks.
+//   - weights: [tap][ci][co] with channel co = 16*cb + c at word 4*c + cb of
+//     its 64-word row, so one 16-byte LDS read gives a lane the A operands of
+//     all four 16-channel blocks.
 //
 // Epilogue (fused): the region is written to LDS as sgn*(y) (sgn = -1 when
 // scale < 0) with -inf where the pool's padding lies, each thread takes the
@@ -51,22 +51,35 @@ constexpr int kThreads = 256;   // 4 waves
 constexpr int kCoTile = 64;     // output channels per workgroup
 constexpr int kPix = 256;       // region pixels per workgroup (4 waves x 4 x 16)
 constexpr int kYS = 260;        // LDS row stride of the staged region (4 mod 64 words)
-constexpr int kFillBatch = 8;   // global loads in flight per thread during a fill
+constexpr int kMaxPR = 28;      // patch values per thread per fill pass
+constexpr int kKB = 9;          // 16-wide weight k blocks per channel group per fill pass
+constexpr int kMaxWR = 4 * kKB; // weights per thread per fill pass
 
 struct GenGeom {
     int Cin, H, W, Cout, kH, kW, cs, cp, cd, OH, OW;
     int pk, ps, pp, pd, PH, PW;        // pool (plain conv: 1, 1, 0, 1, OH, OW)
     int PTH, PTW, CR, CC, IR, IC, CK, PSZ;
+    int SW, lgSW, CPL, npass;          // patch fill: segment width, log2, segments per row
     int tiles_h, tiles_w, co_tiles;
     float scale;
+    // ceil(2^32 / d) for the divisions by IR, CPL, CC, PTW and PTH*PTW (0 when d == 1);
+    // the host checks n * d < 2^32 for every dividend n, which makes them exact.
+    uint32_t mIR, mCPL, mCC, mPTW, mPT;
 };
+
+// floor(n / d) for 0 <= n, n * d < 2^32, with m = ceil(2^32 / d) (m = 0 encodes d = 1).
+__device__ __forceinline__ int fdiv(int n, uint32_t m) {
+    return m ? (int)__umulhi((uint32_t)n, m) : n;
+}
+
+constexpr int kWRS = 68;        // LDS words per weight row (64 channels + 4: conflict-free fill)
 
 __device__ __forceinline__ float to_f32(float v) { return v; }
 __device__ __forceinline__ float to_f32(uint16_t v) { return bf16_to_f32(v); }
 __device__ __forceinline__ void store_out(float *p, float v) { *p = v; }
 __device__ __forceinline__ void store_out(uint16_t *p, float v) { *p = f32_to_bf16_rne(v); }
 
-template <typename TI, int EPI>
+template <typename TI, int EPI, bool PF>
 __global__ __launch_bounds__(kThreads, 2) void conv_general(
     const TI *__restrict__ x, const TI *__restrict__ w, const float *__restrict__ cbias,
     const float *__restrict__ b2, TI *__restrict__ y, const GenGeom g) {
@@ -100,16 +113,13 @@ __global__ __launch_bounds__(kThreads, 2) void conv_general(
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
         const int p = 16 * (wv + 4 * tt) + c;
-        const int r = p / g.CC, cc = p - (p / g.CC) * g.CC;
+        const int r = fdiv(p, g.mCC), cc = p - r * g.CC;
         off[tt] = p < npix ? r * g.cs * g.IC + cc * g.cs : 0;
         orow[tt] = oh0 + r;
         ocol[tt] = ow0 + cc;
         if (p < npix && orow[tt] >= 0 && orow[tt] < g.OH && ocol[tt] >= 0 && ocol[tt] < g.OW)
             inside |= 1u << tt;
     }
-    int aoff[4];
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) aoff[cb] = grp * kCoTile + (((cb ^ grp) << 4) | c);
 
     f32x4 acc[4][4];
 #pragma unroll
@@ -118,76 +128,159 @@ __global__ __launch_bounds__(kThreads, 2) void conv_general(
         for (int tt = 0; tt < 4; ++tt) acc[cb][tt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
     float *xs = smem;                    // [CK][PSZ]
-    float *ws = smem + g.CK * g.PSZ;     // [T][CK][64] (swizzled)
+    float *ws = smem + g.CK * g.PSZ;     // [CK*T][kWRS]: row k = ci*T + tap of the chunk
+    // Loads use 32-bit element offsets from workgroup-uniform bases (the host keeps
+    // one image and the weight tensor below 2^31 elements), so each in-flight load
+    // holds one VGPR of address.
     const TI *xn = x + (size_t)n * g.Cin * g.H * g.W;
-    const size_t plane = (size_t)g.H * g.W;
-    const int irc = g.IR * g.IC;
-    const int pe = g.CK * irc;           // patch elements per chunk
+    const uint32_t plane = (uint32_t)g.H * (uint32_t)g.W;
     const int ckt = g.CK * T;
-    const int we = kCoTile * ckt;        // weight elements per chunk
+    // Patch fill: the rows (ci, r) of a chunk are cut into segments of SW columns
+    // (SW a power of two <= 64); one wave instruction covers 64/SW segments, lane ->
+    // (segment, column), so loads are coalesced along a row and LDS writes are
+    // consecutive.  Segment s of the chunk goes to instruction s / (4*spi) of wave
+    // (s / spi) % 4.
+    const int spi = 64 >> g.lgSW;
+    const int sub = lane >> g.lgSW;
+    const int scol = lane & (g.SW - 1);
+    const int nseg = g.CK * g.IR * g.CPL;
+    // Weight fill: a wave instruction covers 16 consecutive k (= ci*T + tap) of the
+    // chunk for 4 channels co = cg + 16*cb (lane = 16*cb + kk).  Wave wv takes the
+    // channel groups cg = wv + 4q (q < 4) and walks their k blocks in order, so the
+    // addresses of one group differ by immediates.  The channel sits at word
+    // 4*cg + cb of row k: one 16-byte LDS read gives a lane the A operands of its
+    // four 16-channel blocks, and the 68-word row stride makes the fill's writes
+    // conflict-free.
+    const int wvu = __builtin_amdgcn_readfirstlane(wv);
+    const int wcb = lane >> 4, wkk = lane & 15;
+    const uint32_t wcs = (uint32_t)g.Cin * (uint32_t)T;   // weight elements per channel
 
+    // One pass moves up to kMaxPR patch values and kMaxWR weights per thread through
+    // registers.  With PF (the chunk takes one pass) the next chunk's loads are issued
+    // before the current chunk's MFMA work and stored to LDS after it.
+    float pr[kMaxPR], wr[kMaxWR];
+    // The segment decode is the same for every chunk; an opaque zero keeps the
+    // compiler from hoisting all of it out of the chunk loop (which would hold
+    // several registers per segment for the whole kernel).
+    auto lane_sub = [&]() {
+        int z = 0;
+        asm volatile("" : "+v"(z));
+        return sub + z;
+    };
+    auto load = [&](int c0, int p) {
+        const int kvalid = (g.Cin - c0 < g.CK ? g.Cin - c0 : g.CK) * T;
+        const int sb = lane_sub();
+#pragma unroll
+        for (int j = 0; j < kMaxPR; ++j) {
+            const int s = (wvu + 4 * (p * kMaxPR + j)) * spi + sb;
+            float v = 0.f;
+            if (s < nseg) {
+                const int row = fdiv(s, g.mCPL);
+                const int col = (s - row * g.CPL) * g.SW + scol;
+                const int ci = fdiv(row, g.mIR);
+                const int ih = ih0 + row - ci * g.IR, iw = iw0 + col;
+                if (col < g.IC && c0 + ci < g.Cin && ih >= 0 && ih < g.H && iw >= 0 && iw < g.W)
+                    v = to_f32(xn[(uint32_t)(c0 + ci) * plane + (uint32_t)(ih * g.W + iw)]);
+            }
+            pr[j] = v;
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int co = ct + wvu + 4 * q + 16 * wcb;
+            const TI *wq = w + (uint32_t)(co < g.Cout ? co : 0) * wcs + (uint32_t)(c0 * T + wkk);
+#pragma unroll
+            for (int kb = 0; kb < kKB; ++kb) {
+                const int k = 16 * (p * kKB + kb) + wkk;
+                wr[q * kKB + kb] = (co < g.Cout && k < kvalid) ? to_f32(wq[16 * (p * kKB + kb)]) : 0.f;
+            }
+        }
+    };
+    auto store = [&](int p) {
+        const int sb = lane_sub();
+#pragma unroll
+        for (int j = 0; j < kMaxPR; ++j) {
+            const int s = (wvu + 4 * (p * kMaxPR + j)) * spi + sb;
+            if (s < nseg) {
+                const int row = fdiv(s, g.mCPL);
+                const int col = (s - row * g.CPL) * g.SW + scol;
+                const int ci = fdiv(row, g.mIR);
+                if (col < g.IC) xs[ci * g.PSZ + (row - ci * g.IR) * g.IC + col] = pr[j];
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int kb = 0; kb < kKB; ++kb) {
+                const int k = 16 * (p * kKB + kb) + wkk;
+                if (k < ckt) ws[k * kWRS + (((wvu + 4 * q) << 2) | wcb)] = wr[q * kKB + kb];
+            }
+    };
+
+    if constexpr (PF) load(0, 0);
     for (int c0 = 0; c0 < g.Cin; c0 += g.CK) {
         if (c0 > 0) __syncthreads();     // every wave is done with the previous chunk
-        // ---- input patch: all loads of a batch in flight, then the LDS writes ----
-        for (int e0 = threadIdx.x; e0 < pe; e0 += kThreads * kFillBatch) {
-            float v[kFillBatch];
-            int dst[kFillBatch];
-#pragma unroll
-            for (int i = 0; i < kFillBatch; ++i) {
-                const int e = e0 + i * kThreads;
-                const int ci = e / irc;
-                const int rem = e - ci * irc;
-                const int r = rem / g.IC;
-                const int col = rem - r * g.IC;
-                const int ih = ih0 + r, iw = iw0 + col;
-                const bool ok = e < pe && c0 + ci < g.Cin && ih >= 0 && ih < g.H && iw >= 0 &&
-                                iw < g.W;
-                v[i] = ok ? to_f32(xn[(size_t)(c0 + ci) * plane + (size_t)ih * g.W + iw]) : 0.f;
-                dst[i] = e < pe ? ci * g.PSZ + rem : -1;
+        if constexpr (PF) {
+            store(0);
+        } else {
+            for (int p = 0; p < g.npass; ++p) {
+                load(c0, p);
+                store(p);
             }
-#pragma unroll
-            for (int i = 0; i < kFillBatch; ++i)
-                if (dst[i] >= 0) xs[dst[i]] = v[i];
-        }
-        // ---- weights of the chunk: w[ct+co][c0+ci][tap] -> ws[tap][ci][co ^ swz] ----
-        for (int e0 = threadIdx.x; e0 < we; e0 += kThreads * kFillBatch) {
-            float v[kFillBatch];
-            int dst[kFillBatch];
-#pragma unroll
-            for (int i = 0; i < kFillBatch; ++i) {
-                const int e = e0 + i * kThreads;
-                const int co = e / ckt;
-                const int rem = e - co * ckt;
-                const int ci = rem / T;
-                const int t = rem - ci * T;
-                const bool ok = e < we && ct + co < g.Cout && c0 + ci < g.Cin;
-                v[i] = ok ? to_f32(w[((size_t)(ct + co) * g.Cin + c0 + ci) * T + t]) : 0.f;
-                dst[i] = e < we ? (t * g.CK + ci) * kCoTile + (co ^ ((ci & 3) << 4)) : -1;
-            }
-#pragma unroll
-            for (int i = 0; i < kFillBatch; ++i)
-                if (dst[i] >= 0) ws[dst[i]] = v[i];
         }
         __syncthreads();
+        if constexpr (PF) {
+            if (c0 + g.CK < g.Cin) load(c0 + g.CK, 0);
+        }
 
-        // ---- MFMA over the chunk: taps outer, 4-channel groups inner ----
-        for (int t = 0; t < T; ++t) {
-            const int kh = t / g.kW, kw = t - (t / g.kW) * g.kW;
-            const float *xa = xs + grp * g.PSZ + kh * g.cd * g.IC + kw * g.cd;
-            const float *wa = ws + t * g.CK * kCoTile;
-#pragma unroll 2
-            for (int cq = 0; cq < g.CK; cq += 4) {
-                float b[4], a[4];
+        // ---- MFMA over the chunk: step = (tap, 4-channel group cq), taps outer ----
+        // Operands of the next step are read from LDS while the 16 MFMAs of the
+        // current one run.  A is weight row (cq + grp)*T + tap; B is the patch at the
+        // tap's offset (the scalar state cq, tap, kw, tapoff advances with the step).
+        {
+            const float4 *wa4 = (const float4 *)ws + grp * T * (kWRS / 4) + c;
+            const float *xb = xs + grp * g.PSZ;
+            const int nsteps = T * (g.CK >> 2);
+            const int dstep_row = g.cd * g.IC - g.kW * g.cd;   // tapoff change at a new tap row
+            int cq = 0, kw = 0, tapoff = 0, tap = 0;
+            float4 a_c = wa4[0];
+            float b_c[4];
 #pragma unroll
-                for (int tt = 0; tt < 4; ++tt) b[tt] = xa[cq * g.PSZ + off[tt]];
+            for (int tt = 0; tt < 4; ++tt) b_c[tt] = xb[off[tt]];
+            for (int st = 0;; ++st) {
+                int cq_n = cq + 4, kw_n = kw, tap_n = tapoff;
+                if (cq_n == g.CK) {
+                    cq_n = 0;
+                    ++kw_n;
+                    tap_n += g.cd;
+                    if (kw_n == g.kW) {
+                        kw_n = 0;
+                        tap_n += dstep_row;
+                    }
+                }
+                const int tap_i = cq_n == 0 ? tap + 1 : tap;
+                const bool more = st + 1 < nsteps;
+                float4 a_n = a_c;
+                float b_n[4] = {b_c[0], b_c[1], b_c[2], b_c[3]};
+                if (more) {
+                    a_n = wa4[(cq_n * T + tap_i) * (kWRS / 4)];
 #pragma unroll
-                for (int cb = 0; cb < 4; ++cb) a[cb] = wa[cq * kCoTile + aoff[cb]];
+                    for (int tt = 0; tt < 4; ++tt) b_n[tt] = xb[cq_n * g.PSZ + tap_n + off[tt]];
+                }
+                const float av[4] = {a_c.x, a_c.y, a_c.z, a_c.w};
 #pragma unroll
                 for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
                     for (int tt = 0; tt < 4; ++tt)
                         acc[cb][tt] =
-                            __builtin_amdgcn_mfma_f32_16x16x4f32(a[cb], b[tt], acc[cb][tt], 0, 0, 0);
+                            __builtin_amdgcn_mfma_f32_16x16x4f32(av[cb], b_c[tt], acc[cb][tt], 0, 0, 0);
+                if (!more) break;
+                a_c = a_n;
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) b_c[tt] = b_n[tt];
+                cq = cq_n;
+                kw = kw_n;
+                tapoff = tap_n;
+                tap = tap_i;
             }
         }
     }
@@ -231,9 +324,9 @@ __global__ __launch_bounds__(kThreads, 2) void conv_general(
         __syncthreads();
         const int ptile = g.PTH * g.PTW;
         for (int e = threadIdx.x; e < kCoTile * ptile; e += kThreads) {
-            const int col = e / ptile;
+            const int col = fdiv(e, g.mPT);
             const int rem = e - col * ptile;
-            const int pr = rem / g.PTW;
+            const int pr = fdiv(rem, g.mPTW);
             const int pc = rem - pr * g.PTW;
             const int co = ct + col, ph = pr0 + pr, pw = pc0 + pc;
             if (co >= g.Cout || ph >= g.PH || pw >= g.PW) continue;
@@ -268,29 +361,42 @@ bool plan(GenGeom &g, int epi, int &lds_bytes) {
             const int64_t ic = (cc - 1) * g.cs + (int64_t)(g.kW - 1) * g.cd + 1;
             if (ir * ic > (1 << 20)) continue;
             const int psz = pad_words_16mod64((int)(ir * ic));
-            // channel chunk: the largest of 16, 12, 8, 4 (<= Cin rounded up) that fits;
-            // up to 80 KB (two workgroups per CU), else up to 160 KB
-            int ck = 0, lds = 0;
-            for (int lim : {80 * 1024, 160 * 1024}) {
+            int sw = 1, lg = 0;
+            while (sw < ic && sw < 64) { sw *= 2; ++lg; }
+            const int cpl = (int)((ic + sw - 1) / sw);
+            const int spi = 64 / sw;
+            // channel chunk: prefer the largest of 16, 12, 8, 4 (<= Cin rounded up) whose
+            // fill takes one register pass (prefetch) within 80 KB of LDS (two workgroups
+            // per CU); else the largest that fits 80 KB, else 160 KB.
+            int ck = 0, lds = 0, npass = 0;
+            for (int mode = 0; mode < 3 && !ck; ++mode) {
+                const int64_t lim = mode < 2 ? 80 * 1024 : 160 * 1024;
                 for (int k = 16; k >= 4; k -= 4) {
                     if (k > cinp && k > 4) continue;
-                    const int64_t fill = ((int64_t)k * psz + (int64_t)T * k * kCoTile) * 4;
+                    const int64_t fill = ((int64_t)k * psz + (int64_t)T * k * kWRS) * 4;
                     const int64_t need = epi == 0 && fill < kCoTile * kYS * 4 ? kCoTile * kYS * 4 : fill;
-                    if (need <= lim) { ck = k; lds = (int)need; break; }
+                    const int64_t npr = ((int64_t)k * ir * cpl + 4 * spi - 1) / (4 * spi);
+                    const int64_t nkb = ((int64_t)k * T + 15) / 16;
+                    const int64_t np1 = (npr + kMaxPR - 1) / kMaxPR, np2 = (nkb + kKB - 1) / kKB;
+                    const int64_t np = np1 > np2 ? np1 : np2;
+                    if (need > lim || (mode == 0 && np > 1)) continue;
+                    ck = k; lds = (int)need; npass = (int)np;
+                    break;
                 }
-                if (ck) break;
             }
             if (!ck) continue;
             const int64_t tiles = (int64_t)((g.PH + pth - 1) / pth) * ((g.PW + ptw - 1) / ptw);
             const int64_t nchunks = (g.Cin + ck - 1) / ck;
-            // MFMA work is the same per tile; patch re-reads and LDS pressure break ties
-            const int64_t cost = tiles * (1 << 20) * (lds > 80 * 1024 ? 2 : 1) +
+            // MFMA work is the same per tile; exposed fill latency (no prefetch), one
+            // workgroup per CU, and patch re-reads break ties
+            const int64_t cost = tiles * (1 << 20) * (lds > 80 * 1024 ? 2 : 1) * (npass > 1 ? 3 : 2) +
                                  (tiles * nchunks * ck * ir * ic) / 64 - cc;
             if (best_cost < 0 || cost < best_cost) {
                 best_cost = cost;
                 bestg = g;
                 bestg.PTH = pth; bestg.PTW = ptw; bestg.CR = (int)cr; bestg.CC = (int)cc;
                 bestg.IR = (int)ir; bestg.IC = (int)ic; bestg.CK = ck; bestg.PSZ = psz;
+                bestg.SW = sw; bestg.lgSW = lg; bestg.CPL = cpl; bestg.npass = npass;
                 bestg.tiles_h = (g.PH + pth - 1) / pth;
                 bestg.tiles_w = (g.PW + ptw - 1) / ptw;
                 best_lds = lds;
@@ -298,23 +404,44 @@ bool plan(GenGeom &g, int epi, int &lds_bytes) {
         }
     }
     if (best_cost < 0) return false;
+    // exactness of the multiply-shift divisions: every dividend n has n * d < 2^32
+    const int64_t nseg = (int64_t)bestg.CK * bestg.IR * bestg.CPL;
+    const int64_t ptile = (int64_t)bestg.PTH * bestg.PTW;
+    if (nseg * bestg.CPL >= (1ll << 32) || nseg * bestg.IR >= (1ll << 32) ||
+        (int64_t)kPix * bestg.CC >= (1ll << 32) || kCoTile * ptile * ptile >= (1ll << 32))
+        return false;
+    auto magic = [](int64_t d) -> uint32_t {
+        return d <= 1 ? 0u : (uint32_t)(((1ll << 32) + d - 1) / d);
+    };
+    bestg.mIR = magic(bestg.IR);
+    bestg.mCPL = magic(bestg.CPL);
+    bestg.mCC = magic(bestg.CC);
+    bestg.mPTW = magic(bestg.PTW);
+    bestg.mPT = magic(ptile);
     g = bestg;
     lds_bytes = best_lds;
     return true;
 }
 
-template <typename TI, int EPI>
+template <typename TI, int EPI, bool PF>
 int launch_t(const void *x, const void *w, const float *cb, const float *b2, void *y, int N,
              const GenGeom &g, int lds, hipStream_t stream) {
     const uint64_t nblocks = (uint64_t)N * g.tiles_h * g.tiles_w * g.co_tiles;
     if (nblocks > 0x7fffffffull) return PS_ERR_UNSUPPORTED;
     if (lds > 64 * 1024 &&
-        hipFuncSetAttribute((const void *)conv_general<TI, EPI>,
+        hipFuncSetAttribute((const void *)conv_general<TI, EPI, PF>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
         return PS_ERR_HIP;
-    hipLaunchKernelGGL((conv_general<TI, EPI>), dim3((unsigned)nblocks), dim3(kThreads),
+    hipLaunchKernelGGL((conv_general<TI, EPI, PF>), dim3((unsigned)nblocks), dim3(kThreads),
                        (size_t)lds, stream, (const TI *)x, (const TI *)w, cb, b2, (TI *)y, g);
     return hipGetLastError() == hipSuccess ? PS_OK : PS_ERR_HIP;
+}
+
+template <typename TI, int EPI>
+int launch_e(const void *x, const void *w, const float *cb, const float *b2, void *y, int N,
+             const GenGeom &g, int lds, hipStream_t stream) {
+    return g.npass == 1 ? launch_t<TI, EPI, true>(x, w, cb, b2, y, N, g, lds, stream)
+                        : launch_t<TI, EPI, false>(x, w, cb, b2, y, N, g, lds, stream);
 }
 
 }  // namespace
@@ -332,13 +459,15 @@ int launch_conv_general(const void *x, const void *w, const float *conv_bias, co
         g.pk = pk; g.ps = ps_; g.pp = pp; g.pd = pd; g.PH = PH; g.PW = PW; g.scale = scale;
     }
     g.co_tiles = (Cout + kCoTile - 1) / kCoTile;
+    if ((int64_t)Cin * H * W >= (1ll << 31) || (int64_t)Cout * Cin * kH * kW >= (1ll << 31))
+        return PS_ERR_UNSUPPORTED;
     int lds = 0;
     if (!plan(g, epi, lds)) return PS_ERR_UNSUPPORTED;
     if (dtype == PS_BF16)
-        return epi == 1 ? launch_t<uint16_t, 1>(x, w, conv_bias, bias2, y, N, g, lds, stream)
-                        : launch_t<uint16_t, 0>(x, w, conv_bias, bias2, y, N, g, lds, stream);
-    return epi == 1 ? launch_t<float, 1>(x, w, conv_bias, bias2, y, N, g, lds, stream)
-                    : launch_t<float, 0>(x, w, conv_bias, bias2, y, N, g, lds, stream);
+        return epi == 1 ? launch_e<uint16_t, 1>(x, w, conv_bias, bias2, y, N, g, lds, stream)
+                        : launch_e<uint16_t, 0>(x, w, conv_bias, bias2, y, N, g, lds, stream);
+    return epi == 1 ? launch_e<float, 1>(x, w, conv_bias, bias2, y, N, g, lds, stream)
+                    : launch_e<float, 0>(x, w, conv_bias, bias2, y, N, g, lds, stream);
 }
 
 }  // namespace ps
