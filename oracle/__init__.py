@@ -53,6 +53,8 @@ def _load():
     lib.or_conv_tanh_scale_bias_maxpool.argtypes = [p, p, p, p, p] + [i] * 10 + [d] + [i] * 4
     lib.or_conv_tanh_scale_bias_maxpool_points.argtypes = (
         [p, p, p, p] + [i] * 10 + [d] + [i] * 4 + [i64, p, p])
+    lib.or_tanh_scale_bias_maxpool.argtypes = [p, p, p] + [i] * 4 + [d] + [i] * 4
+    lib.or_softmax_bias_scale_sigmoid.argtypes = [p, p, p] + [i] * 4 + [d]
     lib.or_conv_transpose2d.argtypes = [p, p, p, p] + [i] * 10
     lib.or_convT_softmax_bias_scale_sigmoid.argtypes = [p, p, p, p, p] + [i] * 10 + [d]
     lib.or_convT_softmax_bias_scale_sigmoid_pixels.argtypes = (
@@ -148,6 +150,28 @@ def conv_tanh_scale_bias_maxpool_points(c, flat_idx):
         c["N"], c["Cin"], c["H"], c["W"], c["Cout"], c["kH"], c["kW"],
         c["conv_stride"], c["conv_pad"], c["conv_dil"], float(c["scale"]),
         c["pool_k"], ps, c["pool_pad"], c["pool_dil"], idx.shape[0], _ptr(idx), _ptr(out))
+    return out
+
+
+def tanh_scale_bias_maxpool(y, bias2, scale, k, stride=None, pad=0, dil=1):
+    """maxpool(tanh(y) * scale + bias2[c]) of a stored float32 conv output; float64."""
+    y, b2 = _f32(y), _f32(bias2)
+    stride = k if stride is None or stride <= 0 else stride
+    N, C, H, W = y.shape
+    OH, OW = window_out_dim(H, k, stride, pad, dil), window_out_dim(W, k, stride, pad, dil)
+    out = np.zeros((N, C, max(OH, 0), max(OW, 0)), dtype=np.float64)
+    _load().or_tanh_scale_bias_maxpool(_ptr(y), _ptr(b2), _ptr(out), N, C, H, W, float(scale),
+                                       k, stride, pad, dil)
+    return out
+
+
+def softmax_bias_scale_sigmoid(y, bias2, scale):
+    """sigmoid((softmax_c(y) + bias2[c]) * scale) of a stored float32 convT output; float64."""
+    y, b2 = _f32(y), _f32(bias2)
+    N, C, H, W = y.shape
+    out = np.zeros(y.shape, dtype=np.float64)
+    _load().or_softmax_bias_scale_sigmoid(_ptr(y), _ptr(b2), _ptr(out), N, C, H, W,
+                                          float(scale))
     return out
 
 

@@ -228,6 +228,27 @@ void or_conv_tanh_scale_bias_maxpool_points(const float *x, const float *w,
     }
 }
 
+/* Second stage of the l2_p82 page's unfused pipeline, on a stored conv output
+ * y [N,C,H,W] (float): z = tanh(y) * scale + bias2[c] for every element, then
+ * the max-pool (floor mode, -inf padding).  Written order, no reordering. */
+void or_tanh_scale_bias_maxpool(const float *y, const float *bias2, double *out,
+                                int N, int C, int H, int W, double scale,
+                                int k, int s, int p, int d) {
+    int64_t total = (int64_t)N * C * H * W;
+    double *z = (double *)malloc(sizeof(double) * (size_t)total);
+    if (!z) return;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < total; i++) {
+        int c = (int)((i / ((int64_t)H * W)) % C);
+        double t = tanh((double)y[i]);
+        t = t * scale;
+        t = t + (double)bias2[c];
+        z[i] = t;
+    }
+    or_maxpool2d_f64(z, out, N, C, H, W, k, s, p, d);
+    free(z);
+}
+
 /* ConvTranspose2d in scatter form: for every input pixel (n, ci, ih, iw) and
  * every tap (kh, kw), the product x[n,ci,ih,iw] * w[ci,co,kh,kw] is added to
  * out[n,co,oh,ow] with oh = ih*s - p + kh*d, ow = iw*s - p + kw*d, when that
@@ -287,6 +308,16 @@ static void softmax_bias_scale_sigmoid_inplace(double *y, const float *bias2, do
                 v[c * HW] = 1.0 / (1.0 + exp(-t));
             }
         }
+}
+
+/* Second stage of the l2_p91 page's unfused pipeline, on a stored convT
+ * output y [N,C,H,W] (float): the channel softmax and epilogue above. */
+void or_softmax_bias_scale_sigmoid(const float *y, const float *bias2, double *out,
+                                   int N, int C, int H, int W, double scale) {
+    int64_t total = (int64_t)N * C * H * W;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < total; i++) out[i] = (double)y[i];
+    softmax_bias_scale_sigmoid_inplace(out, bias2, scale, N, C, (int64_t)H * W);
 }
 
 void or_convT_softmax_bias_scale_sigmoid(const float *x, const float *w, const float *convT_bias,

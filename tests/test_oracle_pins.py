@@ -243,6 +243,36 @@ def test_monotone_reorder_identity(scale):
     np.testing.assert_allclose(fused, alt, rtol=0, atol=1e-15)
 
 
+# ---------------------------------------- second stage of the unfused conv ---
+@pytest.mark.parametrize("k,st,p,d,scale", [(4, 4, 0, 1, 2.0), (3, 2, 1, 1, 2.0),
+                                             (2, 1, 0, 2, -1.5), (3, 3, 1, 1, 0.0),
+                                             (4, 1, 1, 1, 0.7)])
+def test_tanh_scale_bias_maxpool_matches_torch_chain(k, st, p, d, scale):
+    """The stored-conv-output epilogue + pool against torch fp64 (tanh, *scale, +bias,
+    max_pool2d) on random data."""
+    rng = np.random.default_rng(31)
+    y = (rng.standard_normal((2, 3, 19, 17)) * 2).astype(np.float32)
+    b2 = rng.standard_normal(3).astype(np.float32) * 0.1
+    got = oracle.tanh_scale_bias_maxpool(y, b2, scale, k, st, p, d)
+    z = torch.tanh(_t(y)) * scale + _t(b2).view(1, -1, 1, 1)
+    ref = F.max_pool2d(z, k, st, p, d).numpy()
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-14)
+
+
+def test_two_stage_conv_equals_fused():
+    """The l2_p82 page's unfused pipeline (conv to memory, then epilogue + pool)
+    computes the fused op: oracle stage 2 on the oracle's conv output (rounded to
+    float32, as a stored fp32 intermediate is) agrees with the fused oracle to the
+    rounding of the intermediate."""
+    c = inputgen.random_conv_case(1300, N=2, Cin=5, H=22, W=19, Cout=6, conv_pad=1,
+                                  pool_k=3, pool_stride=2, pool_pad=1)
+    y = oracle.conv2d(c["x"], c["w"], c["conv_bias"], c["conv_stride"], c["conv_pad"],
+                      c["conv_dil"]).astype(np.float32)
+    two = oracle.tanh_scale_bias_maxpool(y, c["bias2"], c["scale"], c["pool_k"],
+                                         c["pool_stride"], c["pool_pad"], c["pool_dil"])
+    np.testing.assert_allclose(two, oracle.conv_tanh_scale_bias_maxpool(c), rtol=0, atol=1e-6)
+
+
 # ------------------------------------------------------- conv transpose 2d ---
 @pytest.mark.parametrize("cfg", [
     dict(N=1, Cin=3, Cout=4, H=5, W=6, k=4, s=2, p=1, op=1, d=1),
@@ -388,6 +418,28 @@ def test_softmax_sums_to_one_and_shift_invariance():
     c2 = dict(c)
     c2["convT_bias"] = (c["convT_bias"] + np.float32(3.0)).astype(np.float32)
     np.testing.assert_allclose(oracle.convT_softmax_bias_scale_sigmoid(c2), out, atol=1e-12)
+
+
+def test_softmax_post_process_matches_torch_chain():
+    """The stored-convT-output post-process against torch fp64 (softmax over dim 1,
+    +bias, *scale, sigmoid)."""
+    rng = np.random.default_rng(32)
+    y = (rng.standard_normal((2, 9, 5, 7)) * 3).astype(np.float32)
+    b2 = rng.standard_normal(9).astype(np.float32) * 0.1
+    got = oracle.softmax_bias_scale_sigmoid(y, b2, -0.8)
+    ref = torch.sigmoid((torch.softmax(_t(y), dim=1) + _t(b2).view(1, -1, 1, 1)) * -0.8)
+    np.testing.assert_allclose(got, ref.numpy(), rtol=0, atol=1e-14)
+
+
+def test_two_stage_convT_equals_fused():
+    """The l2_p91 page's unfused pipeline (convT to memory, then the post-process)
+    computes the fused op, up to the float32 rounding of the stored intermediate."""
+    c = inputgen.random_convT_case(2300, N=2, Cin=4, H=5, W=6, Cout=8)
+    y = oracle.conv_transpose2d(c["x"], c["w"], c["convT_bias"], c["stride"], c["pad"],
+                                c["output_padding"], c["dil"]).astype(np.float32)
+    two = oracle.softmax_bias_scale_sigmoid(y, c["bias2"], c["scale"])
+    np.testing.assert_allclose(two, oracle.convT_softmax_bias_scale_sigmoid(c), rtol=0,
+                               atol=1e-6)
 
 
 def test_online_softmax_recurrence_equals_two_pass():
