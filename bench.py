@@ -10,6 +10,10 @@ synthetic workload, on inputs already resident in HBM:
   convT       x fp32 [128,64,64,64] -> convT 64->128 k4 s2 p1 op1 + softmax + bias + *2
               + sigmoid -> [128,128,129,129]   (136.37 GFLOP over the valid taps)
   conv_bf16   the conv workload with bf16 x, w and output (74.91 GFLOP)
+  conv_2stage the conv workload unfused: ps_conv2d stores the full 254x254 conv output
+              (2.11 GB), then the epilogue + pool kernel reads it back (the pages' baseline)
+  convT_2stage the convT workload unfused: ps_convT2d stores the 1.09 GB output, then
+              the softmax post-process runs in place on it
   conv_general x fp32 [32,64,128,128] -> conv 64->128 k3 p1 + tanh + *2 + bias
               + maxpool k3 s2 p1 (overlapping windows) -> [32,128,64,64]
               (77.31 GFLOP: every 128x128 conv output is read by some window)
@@ -40,6 +44,8 @@ CONV_FLOP = 2 * 72 * 128 * 64 * 252 * 252
 CONV_FLOP_PAGE = 2 * 72 * 128 * 64 * 254 * 254     # the page's count over all 254x254 outputs
 POOL_BYTES = 32 * 64 * 512 * 512 * 4 + 32 * 64 * 511 * 511 * 4
 CONV_GENERAL_FLOP = 2 * 64 * 9 * 32 * 128 * 128 * 128
+CONV_INTER_BYTES = 128 * 64 * 254 * 254 * 4        # the stored conv output of the unfused pipeline
+CONVT_INTER_BYTES = 128 * 128 * 129 * 129 * 4      # the stored convT output
 CONVT_FLOP = 2 * 128 * 64 * 128 * 255 * 255
 CONVT_BYTES = 128 * 64 * 64 * 64 * 4 + 128 * 128 * 129 * 129 * 4 + 64 * 128 * 16 * 4
 
@@ -60,6 +66,8 @@ KERNEL_SOURCES = {
     "maxpool": ["maxpool.hip", "ps_internal.h"],
     "convT": ["convt_softmax.hip", "ps_internal.h"],
     "conv_general": ["conv_general.hip", "ps_internal.h"],
+    "conv_2stage": ["conv_general.hip", "two_stage.hip", "ps_internal.h"],
+    "convT_2stage": ["convt_softmax.hip", "two_stage.hip", "ps_internal.h"],
 }
 
 
@@ -86,7 +94,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (profiling runs)")
-    ap.add_argument("--ops", default="conv,maxpool,convT,conv_bf16,conv_general")
+    ap.add_argument("--ops",
+                    default="conv,maxpool,convT,conv_bf16,conv_general,conv_2stage,convT_2stage")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a 2 GiB device-to-device copy instead (counter calibration)")
     return ap.parse_args()
@@ -179,6 +188,30 @@ def main():
         runs["conv_general"] = lambda xg=xg, wg=wg, cbg=cbg, b2g=b2g, outg=outg: (
             ps.conv_tanh_scale_bias_maxpool(xg, wg, cbg, b2g, 2.0, 3, 2, 1, 1, 1, 1, 1, out=outg))
         del c
+    stages = {}   # op -> list of stage callables (timed one by one)
+    if "conv_2stage" in ops:
+        c = inputgen.workload("conv")
+        x2, w2, cb2, b22 = put(c["x"]), put(c["w"]), put(c["conv_bias"]), put(c["bias2"])
+        inter = torch.empty((128, 64, 254, 254), dtype=torch.float32, device=dev)
+        out2 = torch.empty((128, 64, 63, 63), dtype=torch.float32, device=dev)
+        stages["conv_2stage"] = [
+            lambda x2=x2, w2=w2, cb2=cb2, inter=inter: ps.conv2d(x2, w2, cb2, out=inter),
+            lambda inter=inter, b22=b22, out2=out2: ps.tanh_scale_bias_maxpool(
+                inter, b22, 2.0, 4, out=out2)]
+        del c
+    if "convT_2stage" in ops:
+        c = inputgen.workload("convT")
+        xt2, wt2, cbt2, b2t2 = put(c["x"]), put(c["w"]), put(c["convT_bias"]), put(c["bias2"])
+        intert = torch.empty((128, 128, 129, 129), dtype=torch.float32, device=dev)
+        stages["convT_2stage"] = [
+            lambda xt2=xt2, wt2=wt2, cbt2=cbt2, intert=intert: ps.convT2d(
+                xt2, wt2, cbt2, 2, 1, 1, 1, out=intert),
+            lambda intert=intert, b2t2=b2t2: ps.softmax_bias_scale_sigmoid(
+                intert, b2t2, 2.0, out=intert)]
+        del c
+    for name, fns in stages.items():
+        for si, fn in enumerate(fns):
+            runs[f"{name}#{si}"] = fn
     torch.cuda.synchronize()
     print(f"[bench] inputs ready in {time.time() - t0:.1f}s; ops {list(runs)}",
           file=sys.stderr, flush=True)
@@ -261,6 +294,35 @@ def main():
                          "unit": "TFLOP/s", "frac": ach / PEAK_FP32,
                          "traffic": traffic("conv_general")}}
 
+    if "conv_2stage#0" in runs:
+        m0, m1 = stats("conv_2stage#0")[0], stats("conv_2stage#1")[0]
+        a0 = CONV_FLOP_PAGE / (m0 * 1e-3)
+        b1 = (CONV_INTER_BYTES + 128 * 64 * 63 * 63 * 4) / (m1 * 1e-3)
+        fused = out_ops.get("conv", {}).get("ms_mean")
+        out_ops["conv_2stage"] = {
+            "value": CONV_FLOP / ((m0 + m1) * 1e-3) / 1e9, "unit": "GFLOP/s",
+            "ms_mean": m0 + m1, "stage_ms": [m0, m1],
+            "fusion_speedup": (m0 + m1) / fused if fused else None,
+            "roofline": {"bound": "mfma", "achieved": a0 / 1e12, "peak": PEAK_FP32 / 1e12,
+                         "unit": "TFLOP/s", "frac": a0 / PEAK_FP32, "traffic": None,
+                         "kernel": "conv2d stage (76.1 GFLOP over all 254x254 outputs)"},
+            "stage2_roofline": {"bound": "hbm", "achieved": b1 / 1e9, "peak": PEAK_HBM / 1e9,
+                                "unit": "GB/s", "frac": b1 / PEAK_HBM}}
+    if "convT_2stage#0" in runs:
+        m0, m1 = stats("convT_2stage#0")[0], stats("convT_2stage#1")[0]
+        a0 = CONVT_FLOP / (m0 * 1e-3)
+        b1 = 2 * CONVT_INTER_BYTES / (m1 * 1e-3)
+        fused = out_ops.get("convT", {}).get("ms_mean")
+        out_ops["convT_2stage"] = {
+            "value": CONVT_FLOP / ((m0 + m1) * 1e-3) / 1e9, "unit": "GFLOP/s",
+            "ms_mean": m0 + m1, "stage_ms": [m0, m1],
+            "fusion_speedup": (m0 + m1) / fused if fused else None,
+            "roofline": {"bound": "mfma", "achieved": a0 / 1e12, "peak": PEAK_FP32 / 1e12,
+                         "unit": "TFLOP/s", "frac": a0 / PEAK_FP32, "traffic": None,
+                         "kernel": "convT stage"},
+            "stage2_roofline": {"bound": "hbm", "achieved": b1 / 1e9, "peak": PEAK_HBM / 1e9,
+                                "unit": "GB/s", "frac": b1 / PEAK_HBM}}
+
     head = "conv" if "conv" in out_ops else next(iter(out_ops))
     cpu = None
     if not args.no_cpu_baseline and head == "conv":
@@ -289,6 +351,8 @@ def main():
             "conv_bf16_workload": "conv workload with bf16 x/w/out, fp32 accumulate",
             "conv_general_workload": "conv2d 64->128 k3 p1 + tanh + *2 + bias + maxpool k3 s2 p1, "
                                      "x fp32 [32,64,128,128] -> [32,128,64,64]",
+            "two_stage": "conv_2stage / convT_2stage: the conv and convT workloads unfused "
+                         "(intermediate stored in HBM), for the fusion comparison",
         },
         "roofline": out_ops[head]["roofline"],
         "cpu_baseline": cpu,

@@ -9,6 +9,9 @@
  *   ps_maxpool2d                        MaxPool2d (stride-1 overlapping windows included)
  *   ps_convT_softmax_bias_scale_sigmoid ConvTranspose2d -> softmax over channels
  *                                       -> +bias2[c] -> *scale -> sigmoid, fused
+ *   ps_convT2d                          ConvTranspose2d + bias (unfused first stage)
+ *   ps_tanh_scale_bias_maxpool          tanh/scale/bias + MaxPool2d of a stored conv output
+ *   ps_softmax_bias_scale_sigmoid       channel softmax post-process of a stored convT output
  *
  * The operations and their arguments follow the problem statements of three
  * POPCORNBENCH transcripts (cited by page name):
@@ -152,6 +155,39 @@ int ps_convT_softmax_bias_scale_sigmoid(
     const float *x, const float *w, const float *convT_bias, const float *bias2, float *y,
     int N, int Cin, int H, int W, int Cout, int k, int stride, int pad, int output_padding,
     int dil, float scale, void *stream);
+
+/* ------------------------------------------------ plain transposed conv --- */
+/* The first stage of the l2_p91 page's unfused pipeline (the transposed conv
+ * writes its full output, then a post-processing kernel runs in place on it);
+ * also a plain nn.ConvTranspose2d forward:
+ *   y[n,co,oh,ow] = bias[co] + sum over (ci, ih, iw, kh, kw) with
+ *                   oh = ih*s - p + kh*d, ow = iw*s - p + kw*d of x[n,ci,ih,iw]*w[ci,co,kh,kw]
+ * x [N,Cin,H,W] float32, w [Cin,Cout,k,k] float32, bias [Cout] float32 or NULL,
+ * y [N,Cout,OH,OW] float32.  Supported: the same set as the fused call above. */
+int ps_convT2d(const float *x, const float *w, const float *bias, float *y, int N, int Cin, int H,
+               int W, int Cout, int k, int stride, int pad, int output_padding, int dil,
+               void *stream);
+
+/* -------------------------------------- post-processing of stored outputs --- */
+/* The l2_p82 page's second kernel of the unfused pipeline, on a stored conv output:
+ *   out[n,c,ph,pw] = max over the pool window of tanh(y)*scale + bias2[c]
+ * (floor mode, -inf padding; a window wholly in the padding gives -inf; the window
+ * is reduced before tanh, by the same monotonicity argument as the fused call).
+ * y [N,C,H,W] dtype, bias2 [C] float32, out [N,C,OH,OW] dtype (bf16 rounded to
+ * nearest even).  stride <= 0 means stride = k.  Any window, stride, padding and
+ * dilation.  y and out must not overlap. */
+int ps_tanh_scale_bias_maxpool(const void *y, const float *bias2, void *out, int dtype, int N,
+                               int C, int H, int W, float scale, int k, int stride, int pad,
+                               int dil, void *stream);
+
+/* The l2_p91 page's post-processing kernel of the unfused pipeline, on a stored
+ * transposed-conv output:
+ *   out[n,c,h,w] = 1 / (1 + exp(-(softmax over c of y[n,:,h,w] + bias2[c]) * scale))
+ * y, out [N,C,H,W] float32, bias2 [C] float32.  Any C (up to 128 channels one read
+ * of y, more channels two).  out == y (in place, as on the page) is allowed; any
+ * other overlap is not. */
+int ps_softmax_bias_scale_sigmoid(const float *y, const float *bias2, float *out, int N, int C,
+                                  int H, int W, float scale, void *stream);
 
 #ifdef __cplusplus
 }

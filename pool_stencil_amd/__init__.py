@@ -12,6 +12,9 @@ Operations (same names as the C entry points, without the ps_ prefix):
     conv2d(x, w, bias=None, stride=1, pad=0, dil=1)
     maxpool2d(x, k, stride=None, pad=0, dil=1)
     convT_softmax_bias_scale_sigmoid(x, w, convT_bias, bias2, scale, ...)
+    convT2d(x, w, bias=None, stride=2, pad=1, output_padding=1, dil=1)
+    tanh_scale_bias_maxpool(y, bias2, scale, k, stride=None, pad=0, dil=1)
+    softmax_bias_scale_sigmoid(y, bias2, scale, out=None)   (out=y: in place)
 """
 from __future__ import annotations
 
@@ -28,7 +31,8 @@ PS_F32, PS_BF16 = 0, 1
 EXPORTS = (
     "ps_status_string", "ps_version", "ps_conv2d_out_dim", "ps_pool2d_out_dim",
     "ps_convT2d_out_dim", "ps_conv_tanh_scale_bias_maxpool", "ps_conv2d", "ps_maxpool2d",
-    "ps_convT_softmax_bias_scale_sigmoid",
+    "ps_convT_softmax_bias_scale_sigmoid", "ps_convT2d", "ps_tanh_scale_bias_maxpool",
+    "ps_softmax_bias_scale_sigmoid",
 )
 
 
@@ -60,9 +64,13 @@ def _load() -> ctypes.CDLL:
     lib.ps_conv2d.argtypes = [p, p, p, p] + [i] * 11 + [p]
     lib.ps_maxpool2d.argtypes = [p, p] + [i] * 8 + [p]
     lib.ps_convT_softmax_bias_scale_sigmoid.argtypes = [p, p, p, p, p] + [i] * 10 + [f, p]
+    lib.ps_convT2d.argtypes = [p, p, p, p] + [i] * 10 + [p]
+    lib.ps_tanh_scale_bias_maxpool.argtypes = [p, p, p] + [i] * 5 + [f] + [i] * 4 + [p]
+    lib.ps_softmax_bias_scale_sigmoid.argtypes = [p, p, p] + [i] * 4 + [f, p]
     for name in ("ps_conv2d_out_dim", "ps_pool2d_out_dim", "ps_convT2d_out_dim",
                  "ps_conv_tanh_scale_bias_maxpool", "ps_conv2d", "ps_maxpool2d",
-                 "ps_convT_softmax_bias_scale_sigmoid"):
+                 "ps_convT_softmax_bias_scale_sigmoid", "ps_convT2d",
+                 "ps_tanh_scale_bias_maxpool", "ps_softmax_bias_scale_sigmoid"):
         getattr(lib, name).restype = i
     return lib
 
@@ -256,4 +264,80 @@ def convT_softmax_bias_scale_sigmoid(x, w, convT_bias, bias2, scale, stride=2, p
         stride, pad, output_padding, dil, float(scale), _stream(stream))
     if st != PS_OK:
         raise PsError(st, "ps_convT_softmax_bias_scale_sigmoid")
+    return out
+
+
+def convT2d(x, w, bias=None, stride=2, pad=1, output_padding=1, dil=1, out=None, stream=None):
+    """ConvTranspose2d + bias: x [N,Cin,H,W] float32, w [Cin,Cout,k,k] float32."""
+    torch = _torch()
+    _check(x, "x", (torch.float32,))
+    _check(w, "w", (torch.float32,), x.device)
+    _check(bias, "bias", (torch.float32,), x.device)
+    N, Cin, H, W = x.shape
+    Cin_w, Cout, k, k2 = w.shape
+    if Cin_w != Cin or k != k2:
+        raise ValueError("w must be [Cin, Cout, k, k]")
+    if bias is not None and bias.numel() != Cout:
+        raise ValueError("bias must hold Cout elements")
+    OH = convT2d_out_dim(H, k, stride, pad, output_padding, dil)
+    OW = convT2d_out_dim(W, k, stride, pad, output_padding, dil)
+    if out is None:
+        out = torch.empty((N, Cout, OH, OW), dtype=torch.float32, device=x.device)
+    else:
+        _check(out, "out", (torch.float32,), x.device)
+        if tuple(out.shape) != (N, Cout, OH, OW):
+            raise ValueError(f"out has shape {tuple(out.shape)}, expected {(N, Cout, OH, OW)}")
+    st = _lib.ps_convT2d(_ptr(x), _ptr(w), _ptr(bias), _ptr(out), N, Cin, H, W, Cout, k, stride,
+                         pad, output_padding, dil, _stream(stream))
+    if st != PS_OK:
+        raise PsError(st, "ps_convT2d")
+    return out
+
+
+def tanh_scale_bias_maxpool(y, bias2, scale, k, stride=None, pad=0, dil=1, out=None,
+                            stream=None):
+    """maxpool(tanh(y) * scale + bias2[c]) of a stored conv output y [N,C,H,W]
+    (float32 or bfloat16; output in y's dtype)."""
+    torch = _torch()
+    _check(y, "y", (torch.float32, torch.bfloat16))
+    _check(bias2, "bias2", (torch.float32,), y.device)
+    N, C, H, W = y.shape
+    if bias2.numel() != C:
+        raise ValueError("bias2 must hold C elements")
+    OH = pool2d_out_dim(H, k, stride, pad, dil)
+    OW = pool2d_out_dim(W, k, stride, pad, dil)
+    if out is None:
+        out = torch.empty((N, C, OH, OW), dtype=y.dtype, device=y.device)
+    else:
+        _check(out, "out", (y.dtype,), y.device)
+        if tuple(out.shape) != (N, C, OH, OW):
+            raise ValueError(f"out has shape {tuple(out.shape)}, expected {(N, C, OH, OW)}")
+    dtype = PS_BF16 if y.dtype == torch.bfloat16 else PS_F32
+    st = _lib.ps_tanh_scale_bias_maxpool(_ptr(y), _ptr(bias2), _ptr(out), dtype, N, C, H, W,
+                                         float(scale), k, 0 if stride is None else stride, pad,
+                                         dil, _stream(stream))
+    if st != PS_OK:
+        raise PsError(st, "ps_tanh_scale_bias_maxpool")
+    return out
+
+
+def softmax_bias_scale_sigmoid(y, bias2, scale, out=None, stream=None):
+    """sigmoid((softmax over channels of y + bias2[c]) * scale) of a stored float32
+    y [N,C,H,W]; pass out=y to run in place."""
+    torch = _torch()
+    _check(y, "y", (torch.float32,))
+    _check(bias2, "bias2", (torch.float32,), y.device)
+    N, C, H, W = y.shape
+    if bias2.numel() != C:
+        raise ValueError("bias2 must hold C elements")
+    if out is None:
+        out = torch.empty_like(y)
+    else:
+        _check(out, "out", (torch.float32,), y.device)
+        if out.shape != y.shape:
+            raise ValueError(f"out has shape {tuple(out.shape)}, expected {tuple(y.shape)}")
+    st = _lib.ps_softmax_bias_scale_sigmoid(_ptr(y), _ptr(bias2), _ptr(out), N, C, H, W,
+                                            float(scale), _stream(stream))
+    if st != PS_OK:
+        raise PsError(st, "ps_softmax_bias_scale_sigmoid")
     return out

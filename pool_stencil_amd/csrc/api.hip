@@ -174,4 +174,51 @@ int ps_convT_softmax_bias_scale_sigmoid(const float *x, const float *w, const fl
                                     scale, (hipStream_t)stream);
 }
 
+int ps_convT2d(const float *x, const float *w, const float *bias, float *y, int N, int Cin, int H,
+               int W, int Cout, int k, int stride, int pad, int output_padding, int dil,
+               void *stream) {
+    if (!x || !w || !y) return PS_ERR_NULL;
+    if (N < 1 || Cin < 1 || H < 1 || W < 1 || Cout < 1) return PS_ERR_SHAPE;
+    int OH, OW;
+    int st = ps_convT2d_out_dim(H, k, stride, pad, output_padding, dil, &OH);
+    if (st != PS_OK) return st;
+    st = ps_convT2d_out_dim(W, k, stride, pad, output_padding, dil, &OW);
+    if (st != PS_OK) return st;
+    if (too_big(N, Cin, H, W) || too_big(N, Cout, OH, OW) || too_big(Cin, Cout, k, k))
+        return PS_ERR_SHAPE;
+    if (k != 4 || stride != 2 || pad != 1 || dil != 1) return PS_ERR_UNSUPPORTED;
+    if (Cout % 16 != 0 || Cout > 128 || Cin > 256) return PS_ERR_UNSUPPORTED;
+    if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return PS_ERR_ALIGN;
+    return ps::launch_convT(x, w, bias, y, N, Cin, H, W, Cout, OH, OW, (hipStream_t)stream);
+}
+
+int ps_tanh_scale_bias_maxpool(const void *y, const float *bias2, void *out, int dtype, int N,
+                               int C, int H, int W, float scale, int k, int stride, int pad,
+                               int dil, void *stream) {
+    if (!y || !bias2 || !out) return PS_ERR_NULL;
+    if (dtype != PS_F32 && dtype != PS_BF16) return PS_ERR_PARAM;
+    if (N < 1 || C < 1 || H < 1 || W < 1) return PS_ERR_SHAPE;
+    if (k < 1 || dil < 1 || pad < 0) return PS_ERR_PARAM;
+    if (stride <= 0) stride = k;
+    int OH, OW;
+    int st = ps_pool2d_out_dim(H, k, stride, pad, dil, &OH);
+    if (st != PS_OK) return st;
+    st = ps_pool2d_out_dim(W, k, stride, pad, dil, &OW);
+    if (st != PS_OK) return st;
+    if (too_big(N, C, H, W) || too_big(N, C, OH, OW)) return PS_ERR_SHAPE;
+    if (!aligned16(y) || !aligned16(out)) return PS_ERR_ALIGN;
+    return ps::launch_tanh_scale_bias_maxpool(y, bias2, out, dtype, N, C, H, W, OH, OW, scale, k,
+                                              stride, pad, dil, (hipStream_t)stream);
+}
+
+int ps_softmax_bias_scale_sigmoid(const float *y, const float *bias2, float *out, int N, int C,
+                                  int H, int W, float scale, void *stream) {
+    if (!y || !bias2 || !out) return PS_ERR_NULL;
+    if (N < 1 || C < 1 || H < 1 || W < 1) return PS_ERR_SHAPE;
+    if (too_big(N, C, H, W)) return PS_ERR_SHAPE;
+    if (!aligned16(y) || !aligned16(out)) return PS_ERR_ALIGN;
+    return ps::launch_softmax_bias_scale_sigmoid(y, bias2, out, N, C, H, W, scale,
+                                                 (hipStream_t)stream);
+}
+
 }  // extern "C"

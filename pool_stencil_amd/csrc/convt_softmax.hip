@@ -43,7 +43,10 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 512;  // 8 waves: two per SIMD
 
-template <int MT, int NQ>
+// SOFTMAX = false: the same transposed conv with the epilogue left out (the
+// stored intermediate of the page's unfused pipeline, or a plain
+// ConvTranspose2d + bias).
+template <int MT, int NQ, bool SOFTMAX>
 __global__ __launch_bounds__(kThreads) void convT_softmax_f32(
     const float *__restrict__ x, const float *__restrict__ w, const float *__restrict__ cbias,
     const float *__restrict__ b2, float *__restrict__ y, int N, int Cin, int H, int W, int OH,
@@ -81,7 +84,7 @@ __global__ __launch_bounds__(kThreads) void convT_softmax_f32(
     }
     for (int e = threadIdx.x; e < COUT; e += kThreads) {
         lcb[e] = cbias ? cbias[e] : 0.f;
-        lb2[e] = b2[e];
+        if constexpr (SOFTMAX) lb2[e] = b2[e];  // b2 is NULL without the softmax epilogue
     }
     __syncthreads();
     (void)Cin4;
@@ -165,6 +168,21 @@ __global__ __launch_bounds__(kThreads) void convT_softmax_f32(
         if (cl < Cq) compute(cl, bA);
 
         // ---- epilogue: D row 4G + r of tile mt = channel 16mt + 4G + r ----
+        if constexpr (!SOFTMAX) {
+#pragma unroll
+            for (int nq = 0; nq < NQ; ++nq)
+                if (pok[nq]) {
+                    float *yo = y + obase[nq];
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int co = 16 * mt + 4 * G + r;
+                            yo[(size_t)co * oplane] = acc[mt][nq][r] + lcb[co];
+                        }
+                }
+            continue;
+        }
 #pragma unroll
         for (int nq = 0; nq < NQ; ++nq) {
             float mx = -INFINITY;
@@ -204,7 +222,7 @@ __global__ __launch_bounds__(kThreads) void convT_softmax_f32(
     }
 }
 
-template <int MT>
+template <int MT, bool SOFTMAX>
 int launch_mt(const float *x, const float *w, const float *cb, const float *b2, float *y, int N,
               int Cin, int H, int W, int OH, int OW, float scale, hipStream_t stream) {
     constexpr int NQ = 2;
@@ -221,17 +239,33 @@ int launch_mt(const float *x, const float *w, const float *cb, const float *b2, 
     int wg_per_class = (ncu + 3) / 4;
     wg_per_class = ((wg_per_class + 7) / 8) * 8;
     const int nblocks = 4 * wg_per_class;
-    static bool attr_set[9] = {false};
-    if (!attr_set[MT]) {
-        if (hipFuncSetAttribute((const void *)convT_softmax_f32<MT, NQ>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)lds_bytes > 65536 ? 160 * 1024 : 65536) != hipSuccess)
-            return PS_ERR_HIP;
-        attr_set[MT] = true;
-    }
-    hipLaunchKernelGGL((convT_softmax_f32<MT, NQ>), dim3(nblocks), dim3(kThreads), lds_bytes,
-                       stream, x, w, cb, b2, y, N, Cin, H, W, OH, OW, scale, Cq, wg_per_class);
+    // a per-device function attribute, so it is set on every launch
+    if (lds_bytes > 65536 &&
+        hipFuncSetAttribute((const void *)convT_softmax_f32<MT, NQ, SOFTMAX>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes) !=
+            hipSuccess)
+        return PS_ERR_HIP;
+    hipLaunchKernelGGL((convT_softmax_f32<MT, NQ, SOFTMAX>), dim3(nblocks), dim3(kThreads),
+                       lds_bytes, stream, x, w, cb, b2, y, N, Cin, H, W, OH, OW, scale, Cq,
+                       wg_per_class);
     return hipGetLastError() == hipSuccess ? PS_OK : PS_ERR_HIP;
+}
+
+template <bool SOFTMAX>
+int launch_cout(const float *x, const float *w, const float *cb, const float *b2, float *y, int N,
+                int Cin, int H, int W, int Cout, int OH, int OW, float scale,
+                hipStream_t stream) {
+    switch (Cout / 16) {
+        case 1: return launch_mt<1, SOFTMAX>(x, w, cb, b2, y, N, Cin, H, W, OH, OW, scale, stream);
+        case 2: return launch_mt<2, SOFTMAX>(x, w, cb, b2, y, N, Cin, H, W, OH, OW, scale, stream);
+        case 3: return launch_mt<3, SOFTMAX>(x, w, cb, b2, y, N, Cin, H, W, OH, OW, scale, stream);
+        case 4: return launch_mt<4, SOFTMAX>(x, w, cb, b2, y, N, Cin, H, W, OH, OW, scale, stream);
+        case 5: return launch_mt<5, SOFTMAX>(x, w, cb, b2, y, N, Cin, H, W, OH, OW, scale, stream);
+        case 6: return launch_mt<6, SOFTMAX>(x, w, cb, b2, y, N, Cin, H, W, OH, OW, scale, stream);
+        case 7: return launch_mt<7, SOFTMAX>(x, w, cb, b2, y, N, Cin, H, W, OH, OW, scale, stream);
+        case 8: return launch_mt<8, SOFTMAX>(x, w, cb, b2, y, N, Cin, H, W, OH, OW, scale, stream);
+    }
+    return PS_ERR_UNSUPPORTED;
 }
 
 }  // namespace
@@ -239,17 +273,14 @@ int launch_mt(const float *x, const float *w, const float *cb, const float *b2, 
 int launch_convT_softmax(const float *x, const float *w, const float *convT_bias,
                          const float *bias2, float *y, int N, int Cin, int H, int W, int Cout,
                          int OH, int OW, float scale, hipStream_t stream) {
-    switch (Cout / 16) {
-        case 1: return launch_mt<1>(x, w, convT_bias, bias2, y, N, Cin, H, W, OH, OW, scale, stream);
-        case 2: return launch_mt<2>(x, w, convT_bias, bias2, y, N, Cin, H, W, OH, OW, scale, stream);
-        case 3: return launch_mt<3>(x, w, convT_bias, bias2, y, N, Cin, H, W, OH, OW, scale, stream);
-        case 4: return launch_mt<4>(x, w, convT_bias, bias2, y, N, Cin, H, W, OH, OW, scale, stream);
-        case 5: return launch_mt<5>(x, w, convT_bias, bias2, y, N, Cin, H, W, OH, OW, scale, stream);
-        case 6: return launch_mt<6>(x, w, convT_bias, bias2, y, N, Cin, H, W, OH, OW, scale, stream);
-        case 7: return launch_mt<7>(x, w, convT_bias, bias2, y, N, Cin, H, W, OH, OW, scale, stream);
-        case 8: return launch_mt<8>(x, w, convT_bias, bias2, y, N, Cin, H, W, OH, OW, scale, stream);
-    }
-    return PS_ERR_UNSUPPORTED;
+    return launch_cout<true>(x, w, convT_bias, bias2, y, N, Cin, H, W, Cout, OH, OW, scale,
+                             stream);
+}
+
+int launch_convT(const float *x, const float *w, const float *convT_bias, float *y, int N,
+                 int Cin, int H, int W, int Cout, int OH, int OW, hipStream_t stream) {
+    return launch_cout<false>(x, w, convT_bias, nullptr, y, N, Cin, H, W, Cout, OH, OW, 1.f,
+                              stream);
 }
 
 }  // namespace ps

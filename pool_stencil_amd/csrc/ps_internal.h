@@ -32,6 +32,17 @@ int launch_convT_softmax(const float *x, const float *w, const float *convT_bias
                          const float *bias2, float *y, int N, int Cin, int H, int W, int Cout,
                          int OH, int OW, float scale, hipStream_t stream);
 
+// The same transposed conv without the softmax epilogue (y = convT + bias).
+int launch_convT(const float *x, const float *w, const float *convT_bias, float *y, int N,
+                 int Cin, int H, int W, int Cout, int OH, int OW, hipStream_t stream);
+
+// Post-processing stages of the unfused pipelines.
+int launch_tanh_scale_bias_maxpool(const void *y, const float *bias2, void *out, int dtype, int N,
+                                   int C, int H, int W, int OH, int OW, float scale, int k, int s,
+                                   int p, int d, hipStream_t stream);
+int launch_softmax_bias_scale_sigmoid(const float *y, const float *bias2, float *out, int N,
+                                      int C, int H, int W, float scale, hipStream_t stream);
+
 // fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN).
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     uint32_t u = __float_as_uint(f);

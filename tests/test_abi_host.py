@@ -163,3 +163,42 @@ def test_convT_validation(ps):
     assert _convT(lib, Cout=24) == ps.PS_ERR_UNSUPPORTED
     assert _convT(lib, Cout=144) == ps.PS_ERR_UNSUPPORTED
     assert _convT(lib, x=MISALIGNED) == ps.PS_ERR_ALIGN
+
+
+def test_convT2d_validation(ps):
+    lib = ps.lib()
+
+    def call(x=FAKE, w=FAKE, b=None, y=FAKE, N=1, Cin=64, H=8, W=8, Cout=128, k=4, s=2, p=1,
+             op=1, d=1):
+        return lib.ps_convT2d(x, w, b, y, N, Cin, H, W, Cout, k, s, p, op, d, None)
+
+    assert call(y=None) == ps.PS_ERR_NULL
+    assert call(H=0) == ps.PS_ERR_SHAPE
+    assert call(op=2) == ps.PS_ERR_PARAM
+    assert call(k=3) == ps.PS_ERR_UNSUPPORTED
+    assert call(Cout=40) == ps.PS_ERR_UNSUPPORTED
+    assert call(x=MISALIGNED) == ps.PS_ERR_ALIGN
+
+
+def test_post_process_validation(ps):
+    lib = ps.lib()
+
+    def pool(y=FAKE, b2=FAKE, out=FAKE, dtype=0, N=1, C=4, H=16, W=16, scale=2.0, k=4, s=0,
+             p=0, d=1):
+        return lib.ps_tanh_scale_bias_maxpool(y, b2, out, dtype, N, C, H, W, scale, k, s, p, d,
+                                              None)
+
+    assert pool(b2=None) == ps.PS_ERR_NULL
+    assert pool(dtype=5) == ps.PS_ERR_PARAM
+    assert pool(k=0) == ps.PS_ERR_PARAM
+    assert pool(d=0) == ps.PS_ERR_PARAM
+    assert pool(H=3, p=0) == ps.PS_ERR_SHAPE
+    assert pool(out=MISALIGNED) == ps.PS_ERR_ALIGN
+
+    def sm(y=FAKE, b2=FAKE, out=FAKE, N=1, C=128, H=8, W=8, scale=2.0):
+        return lib.ps_softmax_bias_scale_sigmoid(y, b2, out, N, C, H, W, scale, None)
+
+    assert sm(y=None) == ps.PS_ERR_NULL
+    assert sm(C=0) == ps.PS_ERR_SHAPE
+    assert sm(N=1 << 20, C=1 << 20) == ps.PS_ERR_SHAPE
+    assert sm(y=MISALIGNED) == ps.PS_ERR_ALIGN
