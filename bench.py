@@ -10,6 +10,8 @@ synthetic workload, on inputs already resident in HBM:
   convT       x fp32 [128,64,64,64] -> convT 64->128 k4 s2 p1 op1 + softmax + bias + *2
               + sigmoid -> [128,128,129,129]   (136.37 GFLOP over the valid taps)
   conv_bf16   the conv workload with bf16 x, w and output (74.91 GFLOP)
+  convT_bf16  the convT workload with bf16 x, w and output (fp32 accumulation); bound by
+              its HBM bytes (0.613 GB) more than by its 136.37 GFLOP at the bf16 peak
   conv_2stage the conv workload unfused: ps_conv2d stores the full 254x254 conv output
               (2.11 GB), then the epilogue + pool kernel reads it back (the pages' baseline)
   convT_2stage the convT workload unfused: ps_convT2d stores the 1.09 GB output, then
@@ -48,6 +50,7 @@ CONV_INTER_BYTES = 128 * 64 * 254 * 254 * 4        # the stored conv output of t
 CONVT_INTER_BYTES = 128 * 128 * 129 * 129 * 4      # the stored convT output
 CONVT_FLOP = 2 * 128 * 64 * 128 * 255 * 255
 CONVT_BYTES = 128 * 64 * 64 * 64 * 4 + 128 * 128 * 129 * 129 * 4 + 64 * 128 * 16 * 4
+CONVT_BF16_BYTES = 128 * 64 * 64 * 64 * 2 + 128 * 128 * 129 * 129 * 2 + 64 * 128 * 16 * 2
 
 # HBM bytes per launch, from two rocprofv3 --pmc passes over this script (FETCH_SIZE,
 # then WRITE_SIZE, KiB per dispatch), each scaled by what the same counter reads for a
@@ -66,6 +69,7 @@ KERNEL_SOURCES = {
     "maxpool": ["maxpool.hip", "ps_internal.h"],
     "convT": ["convt_softmax.hip", "ps_internal.h"],
     "conv_general": ["conv_general.hip", "ps_internal.h"],
+    "convT_bf16": ["convt_softmax_bf16.hip", "ps_internal.h"],
     "conv_2stage": ["conv_general.hip", "two_stage.hip", "ps_internal.h"],
     "convT_2stage": ["convt_softmax.hip", "two_stage.hip", "ps_internal.h"],
 }
@@ -95,7 +99,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (profiling runs)")
     ap.add_argument("--ops",
-                    default="conv,maxpool,convT,conv_bf16,conv_general,conv_2stage,convT_2stage")
+                    default="conv,maxpool,convT,conv_bf16,conv_general,convT_bf16,conv_2stage,"
+                            "convT_2stage")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a 2 GiB device-to-device copy instead (counter calibration)")
     return ap.parse_args()
@@ -187,6 +192,15 @@ def main():
         outg = torch.empty((32, 128, 64, 64), dtype=torch.float32, device=dev)
         runs["conv_general"] = lambda xg=xg, wg=wg, cbg=cbg, b2g=b2g, outg=outg: (
             ps.conv_tanh_scale_bias_maxpool(xg, wg, cbg, b2g, 2.0, 3, 2, 1, 1, 1, 1, 1, out=outg))
+        del c
+    if "convT_bf16" in ops:
+        c = inputgen.workload("convT_bf16")
+        xtb = put(c["x_bits"].view(np.int16)).view(torch.bfloat16)
+        wtb = put(c["w_bits"].view(np.int16)).view(torch.bfloat16)
+        cbtb, b2tb = put(c["convT_bias"]), put(c["bias2"])
+        outtb = torch.empty((128, 128, 129, 129), dtype=torch.bfloat16, device=dev)
+        runs["convT_bf16"] = lambda xtb=xtb, wtb=wtb, cbtb=cbtb, b2tb=b2tb, outtb=outtb: (
+            ps.convT_softmax_bias_scale_sigmoid(xtb, wtb, cbtb, b2tb, 2.0, 2, 1, 1, 1, out=outtb))
         del c
     stages = {}   # op -> list of stage callables (timed one by one)
     if "conv_2stage" in ops:
@@ -294,6 +308,15 @@ def main():
                          "unit": "TFLOP/s", "frac": ach / PEAK_FP32,
                          "traffic": traffic("conv_general")}}
 
+    if "convT_bf16" in runs:
+        mean, med, mn = stats("convT_bf16")
+        bw = CONVT_BF16_BYTES / (mean * 1e-3)
+        out_ops["convT_bf16"] = {
+            "value": CONVT_FLOP / (mean * 1e-3) / 1e9, "unit": "GFLOP/s", "ms_mean": mean,
+            "ms_median": med, "ms_min": mn, "gflop_per_launch": CONVT_FLOP / 1e9,
+            "frac_of_bf16_peak": CONVT_FLOP / (mean * 1e-3) / PEAK_BF16,
+            "roofline": {"bound": "hbm", "achieved": bw / 1e9, "peak": PEAK_HBM / 1e9,
+                         "unit": "GB/s", "frac": bw / PEAK_HBM, "traffic": traffic("convT_bf16")}}
     if "conv_2stage#0" in runs:
         m0, m1 = stats("conv_2stage#0")[0], stats("conv_2stage#1")[0]
         a0 = CONV_FLOP_PAGE / (m0 * 1e-3)
@@ -351,6 +374,7 @@ def main():
             "conv_bf16_workload": "conv workload with bf16 x/w/out, fp32 accumulate",
             "conv_general_workload": "conv2d 64->128 k3 p1 + tanh + *2 + bias + maxpool k3 s2 p1, "
                                      "x fp32 [32,64,128,128] -> [32,128,64,64]",
+            "convT_bf16_workload": "convT workload with bf16 x/w/out, fp32 accumulate",
             "two_stage": "conv_2stage / convT_2stage: the conv and convT workloads unfused "
                          "(intermediate stored in HBM), for the fusion comparison",
         },

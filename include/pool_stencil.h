@@ -9,6 +9,7 @@
  *   ps_maxpool2d                        MaxPool2d (stride-1 overlapping windows included)
  *   ps_convT_softmax_bias_scale_sigmoid ConvTranspose2d -> softmax over channels
  *                                       -> +bias2[c] -> *scale -> sigmoid, fused
+ *   ps_convT_softmax_bias_scale_sigmoid_bf16   the same with bf16 tensors
  *   ps_convT2d                          ConvTranspose2d + bias (unfused first stage)
  *   ps_tanh_scale_bias_maxpool          tanh/scale/bias + MaxPool2d of a stored conv output
  *   ps_softmax_bias_scale_sigmoid       channel softmax post-process of a stored convT output
@@ -153,6 +154,19 @@ int ps_maxpool2d(const float *x, float *y, int N, int C, int H, int W, int k, in
  * Cout a multiple of 16 with 16 <= Cout <= 128, 1 <= Cin <= 256. */
 int ps_convT_softmax_bias_scale_sigmoid(
     const float *x, const float *w, const float *convT_bias, const float *bias2, float *y,
+    int N, int Cin, int H, int W, int Cout, int k, int stride, int pad, int output_padding,
+    int dil, float scale, void *stream);
+
+/* The same fused operation with bfloat16 x, w and y (uint16 bit patterns), fp32
+ * products and accumulation, fp32 softmax and epilogue, y rounded to nearest even.
+ * (The l2_p91 page considers reduced precision for this problem and keeps fp32;
+ * this variant runs the GEMM on the bf16 matrix cores.)  convT_bias and bias2 are
+ * float32.  Supported: k = 4, stride = 2, pad = 1, dil = 1, output_padding in
+ * {0, 1}, Cout in {32, 64, 96, 128}, 2*Cout*(4*Cp + 8)*2 + 8*Cout <= 160 KB
+ * with Cp = Cin rounded up to a multiple of 8 (Cout = 128) or 16 (else), i.e.
+ * Cin <= 72 at Cout = 128, <= 144 at Cout = 64; and x below 2^30 elements. */
+int ps_convT_softmax_bias_scale_sigmoid_bf16(
+    const void *x, const void *w, const float *convT_bias, const float *bias2, void *y,
     int N, int Cin, int H, int W, int Cout, int k, int stride, int pad, int output_padding,
     int dil, float scale, void *stream);
 

@@ -105,7 +105,7 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 # ---------------------------------------------------------------------------
 # Workload table.  Index = position in the list of the five workloads.
 # ---------------------------------------------------------------------------
-WORKLOADS = ["tiny_conv", "maxpool", "conv", "convT", "conv_bf16", "conv_general"]
+WORKLOADS = ["tiny_conv", "maxpool", "conv", "convT", "conv_bf16", "conv_general", "convT_bf16"]
 
 
 def _conv_case(idx, N, Cin, H, W, Cout, wdist, b2dist, dtype="f32", N_take=None):
@@ -150,6 +150,10 @@ def workload(name: str) -> dict:
         return _conv_case(idx, 128, 8, 256, 256, 64, "kaiming", "randn0.02")
     if name == "conv_bf16":
         return _conv_case(idx, 128, 8, 256, 256, 64, "kaiming", "randn0.02", dtype="bf16")
+    if name == "convT_bf16":
+        # the convT workload's shapes and distributions, x and w rounded to bf16
+        c = workload("convT")
+        return _bf16_convT(dict(c))
     if name == "convT":
         fan_in = 128 * 16
         x = randn(seed_for(idx, 0), (128, 64, 64, 64))
@@ -190,13 +194,23 @@ def random_conv_case(seed: int, N, Cin, H, W, Cout, kH=3, kW=3, conv_stride=1, c
     return case
 
 
+def _bf16_convT(case):
+    case["dtype"] = "bf16"
+    case["x_bits"] = to_bf16_bits(case["x"])
+    case["w_bits"] = to_bf16_bits(case["w"])
+    case["x"] = bf16_bits_to_f32(case["x_bits"]).reshape(case["x"].shape)
+    case["w"] = bf16_bits_to_f32(case["w_bits"]).reshape(case["w"].shape)
+    return case
+
+
 def random_convT_case(seed: int, N, Cin, H, W, Cout, k=4, stride=2, pad=1, output_padding=1,
-                      dil=1, scale=2.0, convT_bias=True):
+                      dil=1, scale=2.0, convT_bias=True, dtype="f32"):
     fan_in = Cout * k * k
     x = randn(seed, (N, Cin, H, W))
     w = kaiming_uniform(seed + 1, (Cin, Cout, k, k), fan_in)
     cb = kaiming_uniform(seed + 2, (Cout,), fan_in) if convT_bias else None
     b2 = randn(seed + 3, (Cout,), 0.02)
-    return dict(op="convT", dtype="f32", x=x, w=w, convT_bias=cb, bias2=b2,
+    case = dict(op="convT", dtype="f32", x=x, w=w, convT_bias=cb, bias2=b2,
                 N=N, Cin=Cin, H=H, W=W, Cout=Cout, k=k, stride=stride, pad=pad,
                 output_padding=output_padding, dil=dil, scale=scale)
+    return _bf16_convT(case) if dtype == "bf16" else case

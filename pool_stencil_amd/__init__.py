@@ -31,8 +31,8 @@ PS_F32, PS_BF16 = 0, 1
 EXPORTS = (
     "ps_status_string", "ps_version", "ps_conv2d_out_dim", "ps_pool2d_out_dim",
     "ps_convT2d_out_dim", "ps_conv_tanh_scale_bias_maxpool", "ps_conv2d", "ps_maxpool2d",
-    "ps_convT_softmax_bias_scale_sigmoid", "ps_convT2d", "ps_tanh_scale_bias_maxpool",
-    "ps_softmax_bias_scale_sigmoid",
+    "ps_convT_softmax_bias_scale_sigmoid", "ps_convT_softmax_bias_scale_sigmoid_bf16",
+    "ps_convT2d", "ps_tanh_scale_bias_maxpool", "ps_softmax_bias_scale_sigmoid",
 )
 
 
@@ -64,12 +64,14 @@ def _load() -> ctypes.CDLL:
     lib.ps_conv2d.argtypes = [p, p, p, p] + [i] * 11 + [p]
     lib.ps_maxpool2d.argtypes = [p, p] + [i] * 8 + [p]
     lib.ps_convT_softmax_bias_scale_sigmoid.argtypes = [p, p, p, p, p] + [i] * 10 + [f, p]
+    lib.ps_convT_softmax_bias_scale_sigmoid_bf16.argtypes = [p, p, p, p, p] + [i] * 10 + [f, p]
     lib.ps_convT2d.argtypes = [p, p, p, p] + [i] * 10 + [p]
     lib.ps_tanh_scale_bias_maxpool.argtypes = [p, p, p] + [i] * 5 + [f] + [i] * 4 + [p]
     lib.ps_softmax_bias_scale_sigmoid.argtypes = [p, p, p] + [i] * 4 + [f, p]
     for name in ("ps_conv2d_out_dim", "ps_pool2d_out_dim", "ps_convT2d_out_dim",
                  "ps_conv_tanh_scale_bias_maxpool", "ps_conv2d", "ps_maxpool2d",
-                 "ps_convT_softmax_bias_scale_sigmoid", "ps_convT2d",
+                 "ps_convT_softmax_bias_scale_sigmoid",
+                 "ps_convT_softmax_bias_scale_sigmoid_bf16", "ps_convT2d",
                  "ps_tanh_scale_bias_maxpool", "ps_softmax_bias_scale_sigmoid"):
         getattr(lib, name).restype = i
     return lib
@@ -239,10 +241,12 @@ def convT_softmax_bias_scale_sigmoid(x, w, convT_bias, bias2, scale, stride=2, p
                                      output_padding=1, dil=1, out=None, stream=None):
     """sigmoid((softmax_c(conv_transpose2d(x, w, convT_bias)) + bias2[c]) * scale), fused.
 
-    x [N,Cin,H,W] float32, w [Cin,Cout,k,k] float32 (PyTorch's ConvTranspose2d layout)."""
+    x [N,Cin,H,W] and w [Cin,Cout,k,k] (PyTorch's ConvTranspose2d layout) share a
+    dtype, float32 or bfloat16 (bf16: fp32 accumulation, output in bf16); the biases
+    are float32."""
     torch = _torch()
-    _check(x, "x", (torch.float32,))
-    _check(w, "w", (torch.float32,), x.device)
+    _check(x, "x", (torch.float32, torch.bfloat16))
+    _check(w, "w", (x.dtype,), x.device)
     _check(convT_bias, "convT_bias", (torch.float32,), x.device)
     _check(bias2, "bias2", (torch.float32,), x.device)
     N, Cin, H, W = x.shape
@@ -254,16 +258,17 @@ def convT_softmax_bias_scale_sigmoid(x, w, convT_bias, bias2, scale, stride=2, p
     OH = convT2d_out_dim(H, k, stride, pad, output_padding, dil)
     OW = convT2d_out_dim(W, k, stride, pad, output_padding, dil)
     if out is None:
-        out = torch.empty((N, Cout, OH, OW), dtype=torch.float32, device=x.device)
+        out = torch.empty((N, Cout, OH, OW), dtype=x.dtype, device=x.device)
     else:
-        _check(out, "out", (torch.float32,), x.device)
+        _check(out, "out", (x.dtype,), x.device)
         if tuple(out.shape) != (N, Cout, OH, OW):
             raise ValueError(f"out has shape {tuple(out.shape)}, expected {(N, Cout, OH, OW)}")
-    st = _lib.ps_convT_softmax_bias_scale_sigmoid(
-        _ptr(x), _ptr(w), _ptr(convT_bias), _ptr(bias2), _ptr(out), N, Cin, H, W, Cout, k,
-        stride, pad, output_padding, dil, float(scale), _stream(stream))
+    fn = (_lib.ps_convT_softmax_bias_scale_sigmoid_bf16 if x.dtype == torch.bfloat16
+          else _lib.ps_convT_softmax_bias_scale_sigmoid)
+    st = fn(_ptr(x), _ptr(w), _ptr(convT_bias), _ptr(bias2), _ptr(out), N, Cin, H, W, Cout, k,
+            stride, pad, output_padding, dil, float(scale), _stream(stream))
     if st != PS_OK:
-        raise PsError(st, "ps_convT_softmax_bias_scale_sigmoid")
+        raise PsError(st, fn.__name__)
     return out
 
 

@@ -174,6 +174,32 @@ int ps_convT_softmax_bias_scale_sigmoid(const float *x, const float *w, const fl
                                     scale, (hipStream_t)stream);
 }
 
+int ps_convT_softmax_bias_scale_sigmoid_bf16(const void *x, const void *w,
+                                             const float *convT_bias, const float *bias2,
+                                             void *y, int N, int Cin, int H, int W, int Cout,
+                                             int k, int stride, int pad, int output_padding,
+                                             int dil, float scale, void *stream) {
+    if (!x || !w || !bias2 || !y) return PS_ERR_NULL;
+    if (N < 1 || Cin < 1 || H < 1 || W < 1 || Cout < 1) return PS_ERR_SHAPE;
+    int OH, OW;
+    int st = ps_convT2d_out_dim(H, k, stride, pad, output_padding, dil, &OH);
+    if (st != PS_OK) return st;
+    st = ps_convT2d_out_dim(W, k, stride, pad, output_padding, dil, &OW);
+    if (st != PS_OK) return st;
+    if (too_big(N, Cin, H, W) || too_big(N, Cout, OH, OW) || too_big(Cin, Cout, k, k))
+        return PS_ERR_SHAPE;
+    if (k != 4 || stride != 2 || pad != 1 || dil != 1) return PS_ERR_UNSUPPORTED;
+    // both column classes' bf16 weights (2 x Cout x 4*Cin) must fit the LDS of a CU
+    if (Cout % 32 != 0 || Cout > 128 ||
+        (int64_t)2 * Cout * (4 * (Cout == 128 ? (Cin + 7) / 8 * 8 : (Cin + 15) / 16 * 16) + 8) *
+                    2 + 8 * Cout > 160 * 1024)
+        return PS_ERR_UNSUPPORTED;
+    if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return PS_ERR_ALIGN;
+    return ps::launch_convT_softmax_bf16((const uint16_t *)x, (const uint16_t *)w, convT_bias,
+                                         bias2, (uint16_t *)y, N, Cin, H, W, Cout, OH, OW, scale,
+                                         (hipStream_t)stream);
+}
+
 int ps_convT2d(const float *x, const float *w, const float *bias, float *y, int N, int Cin, int H,
                int W, int Cout, int k, int stride, int pad, int output_padding, int dil,
                void *stream) {

@@ -32,6 +32,11 @@ int launch_convT_softmax(const float *x, const float *w, const float *convT_bias
                          const float *bias2, float *y, int N, int Cin, int H, int W, int Cout,
                          int OH, int OW, float scale, hipStream_t stream);
 
+// bf16 x, w and y (uint16 bit patterns), fp32 accumulation; Cout a multiple of 32.
+int launch_convT_softmax_bf16(const uint16_t *x, const uint16_t *w, const float *convT_bias,
+                              const float *bias2, uint16_t *y, int N, int Cin, int H, int W,
+                              int Cout, int OH, int OW, float scale, hipStream_t stream);
+
 // The same transposed conv without the softmax epilogue (y = convT + bias).
 int launch_convT(const float *x, const float *w, const float *convT_bias, float *y, int N,
                  int Cin, int H, int W, int Cout, int OH, int OW, hipStream_t stream);

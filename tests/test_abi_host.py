@@ -202,3 +202,20 @@ def test_post_process_validation(ps):
     assert sm(C=0) == ps.PS_ERR_SHAPE
     assert sm(N=1 << 20, C=1 << 20) == ps.PS_ERR_SHAPE
     assert sm(y=MISALIGNED) == ps.PS_ERR_ALIGN
+
+
+def test_convT_bf16_validation(ps):
+    lib = ps.lib()
+
+    def call(x=FAKE, w=FAKE, cb=None, b2=FAKE, y=FAKE, N=1, Cin=64, H=8, W=8, Cout=128, k=4,
+             s=2, p=1, op=1, d=1, scale=2.0):
+        return lib.ps_convT_softmax_bias_scale_sigmoid_bf16(x, w, cb, b2, y, N, Cin, H, W, Cout,
+                                                            k, s, p, op, d, scale, None)
+
+    assert call(b2=None) == ps.PS_ERR_NULL
+    assert call(W=0) == ps.PS_ERR_SHAPE
+    assert call(op=2) == ps.PS_ERR_PARAM
+    assert call(s=3) == ps.PS_ERR_UNSUPPORTED
+    assert call(Cout=48) == ps.PS_ERR_UNSUPPORTED       # not a multiple of 32
+    assert call(Cin=80) == ps.PS_ERR_UNSUPPORTED        # weights exceed the LDS
+    assert call(y=MISALIGNED) == ps.PS_ERR_ALIGN

@@ -199,13 +199,17 @@ def test_conv_full_workload_sampled(dev, name, tol):
 def _run_convT(c, dev):
     import pool_stencil_amd as ps
     import torch
-    xd, wd = _dev(c["x"], dev), _dev(c["w"], dev)
+    if c["dtype"] == "bf16":
+        xd = _dev(c["x_bits"].view(np.int16), dev).view(torch.bfloat16)
+        wd = _dev(c["w_bits"].view(np.int16), dev).view(torch.bfloat16)
+    else:
+        xd, wd = _dev(c["x"], dev), _dev(c["w"], dev)
     cb = None if c["convT_bias"] is None else _dev(c["convT_bias"], dev)
     b2 = _dev(c["bias2"], dev)
-    out = _canary(oracle.convT_out_shape(c), dev, torch.float32)
+    out = _canary(oracle.convT_out_shape(c), dev, xd.dtype)
     ps.convT_softmax_bias_scale_sigmoid(xd, wd, cb, b2, c["scale"], c["stride"], c["pad"],
                                         c["output_padding"], c["dil"], out=out)
-    return out.cpu().numpy()
+    return out.float().cpu().numpy()
 
 
 CONVT_CASES = [
@@ -227,6 +231,30 @@ def test_convT_small(dev, kw):
     got = _run_convT(c, dev)
     assert not np.isnan(got).any()
     np.testing.assert_allclose(got, ref, rtol=0, atol=F32_TOL)
+
+
+CONVT_BF16_CASES = [
+    dict(N=2, Cin=64, H=9, W=7, Cout=128),
+    dict(N=1, Cin=64, H=16, W=16, Cout=128, output_padding=0),
+    dict(N=3, Cin=13, H=5, W=11, Cout=64),
+    dict(N=1, Cin=4, H=3, W=3, Cout=32),
+    dict(N=1, Cin=1, H=1, W=1, Cout=32),
+    dict(N=2, Cin=64, H=8, W=8, Cout=128, scale=-0.5, convT_bias=False),
+    dict(N=1, Cin=32, H=12, W=20, Cout=96),
+    dict(N=1, Cin=70, H=6, W=70, Cout=128),       # Cin not a multiple of 4; 3 column blocks
+]
+
+
+@pytest.mark.parametrize("kw", CONVT_BF16_CASES)
+def test_convT_bf16_small(dev, kw):
+    """bf16 x/w/output: the oracle runs the fp32 definition on the bf16-rounded inputs;
+    bar abs 2e-2 (outputs lie in (0, 1), where one bf16 ulp is at most 2^-8)."""
+    c = inputgen.random_convT_case(4100, dtype="bf16", **kw)
+    _say("convT bf16", kw, "seed 4100")
+    ref = oracle.convT_softmax_bias_scale_sigmoid(c)
+    got = _run_convT(c, dev)
+    assert not np.isnan(got).any()
+    np.testing.assert_allclose(got, ref, rtol=0, atol=BF16_TOL)
 
 
 def test_convT_full_workload_sampled(dev):
@@ -252,3 +280,20 @@ def test_convT_full_workload_sampled(dev):
     g = got[:4].astype(np.float64)
     sm = np.log(g / (1.0 - g)) / c["scale"] - c["bias2"].astype(np.float64).reshape(1, -1, 1, 1)
     np.testing.assert_allclose(sm.sum(axis=1), 1.0, atol=5e-3)
+
+
+def test_convT_bf16_full_workload_sampled(dev):
+    c = inputgen.workload("convT_bf16")
+    _say("convT_bf16 workload", c["x"].shape)
+    got = _run_convT(c, dev)
+    N, C, OH, OW = got.shape
+    assert (N, C, OH, OW) == (128, 128, 129, 129)
+    assert not np.isnan(got).any()
+    rng = np.random.default_rng(12)
+    pix = rng.choice(N * OH * OW, size=600, replace=False)
+    edge = [(n * OH + oh) * OW + ow for n in (0, 127) for oh in (0, 1, 127, 128)
+            for ow in (0, 1, 63, 64, 127, 128)]
+    pix = np.unique(np.concatenate([pix, np.array(edge, dtype=np.int64)]))
+    ref = oracle.convT_softmax_bias_scale_sigmoid_pixels(c, pix)
+    flat = got.transpose(0, 2, 3, 1).reshape(-1, C)
+    np.testing.assert_allclose(flat[pix], ref, rtol=0, atol=BF16_TOL)
