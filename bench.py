@@ -58,10 +58,12 @@ CONVT_BF16_BYTES = 128 * 64 * 64 * 64 * 2 + 128 * 128 * 129 * 129 * 2 + 64 * 128
 # x1.0.  `src` is the hash of the kernel's sources when the counters were taken; a
 # kernel edited since then reports traffic null.  See profiles/traffic_*.md.
 TRAFFIC = {
-    "conv": {"src": "dc51f5a7b7f8394b", "fetch_bytes": 266847985, "write_bytes": 130658688},
-    "maxpool": {"src": "231157ba21664983", "fetch_bytes": 2336400337, "write_bytes": 2140942016},
-    "convT": {"src": "4756821d0a67bf5e", "fetch_bytes": 757553201, "write_bytes": 2829604224},
-    "conv_bf16": {"src": "dc51f5a7b7f8394b", "fetch_bytes": 136757779, "write_bytes": 83146208},
+    "conv": {"src": "ccea3519e3dc96f0", "fetch_bytes": 266854673, "write_bytes": 130644640},
+    "maxpool": {"src": "f44fd1c7e36e4898", "fetch_bytes": 2336400872, "write_bytes": 2140929824},
+    "convT": {"src": "4c7a01bc82e390b8", "fetch_bytes": 755485730, "write_bytes": 2825737152},
+    "conv_bf16": {"src": "ccea3519e3dc96f0", "fetch_bytes": 136757796, "write_bytes": 83142592},
+    "conv_general": {"src": "b71c9dcee23d6117", "fetch_bytes": 137186207, "write_bytes": 68958208},
+    "convT_bf16": {"src": "acf350b13cdc96cf", "fetch_bytes": 370533792, "write_bytes": 1275527744},
 }
 KERNEL_SOURCES = {
     "conv": ["conv_pool.hip", "ps_internal.h"],
