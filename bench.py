@@ -10,6 +10,10 @@ synthetic workload, on inputs already resident in HBM:
   convT       x fp32 [128,64,64,64] -> convT 64->128 k4 s2 p1 op1 + softmax + bias + *2
               + sigmoid -> [128,128,129,129]   (136.37 GFLOP over the valid taps)
   conv_bf16   the conv workload with bf16 x, w and output (74.91 GFLOP)
+  maxpool_s2  the max-pool input, k3 s2 p1 (downsampling) -> [32,64,256,256]
+              (2.147 GB read + 0.537 GB written)
+  maxpool_d2  the max-pool input, k3 s1 p2 d2 (dilated) -> [32,64,512,512]
+              (2.147 GB read + 2.147 GB written)
   convT_bf16  the convT workload with bf16 x, w and output (fp32 accumulation); bound by
               its HBM bytes (0.613 GB) more than by its 136.37 GFLOP at the bf16 peak
   conv_2stage the conv workload unfused: ps_conv2d stores the full 254x254 conv output
@@ -46,6 +50,8 @@ CONV_FLOP = 2 * 72 * 128 * 64 * 252 * 252
 CONV_FLOP_PAGE = 2 * 72 * 128 * 64 * 254 * 254     # the page's count over all 254x254 outputs
 POOL_BYTES = 32 * 64 * 512 * 512 * 4 + 32 * 64 * 511 * 511 * 4
 CONV_GENERAL_FLOP = 2 * 64 * 9 * 32 * 128 * 128 * 128
+POOL_S2_BYTES = 32 * 64 * 512 * 512 * 4 + 32 * 64 * 256 * 256 * 4
+POOL_D2_BYTES = 2 * 32 * 64 * 512 * 512 * 4
 CONV_INTER_BYTES = 128 * 64 * 254 * 254 * 4        # the stored conv output of the unfused pipeline
 CONVT_INTER_BYTES = 128 * 128 * 129 * 129 * 4      # the stored convT output
 CONVT_FLOP = 2 * 128 * 64 * 128 * 255 * 255
@@ -72,6 +78,8 @@ KERNEL_SOURCES = {
     "convT": ["convt_softmax.hip", "ps_internal.h"],
     "conv_general": ["conv_general.hip", "ps_internal.h"],
     "convT_bf16": ["convt_softmax_bf16.hip", "ps_internal.h"],
+    "maxpool_s2": ["maxpool.hip", "ps_internal.h"],
+    "maxpool_d2": ["maxpool.hip", "ps_internal.h"],
     "conv_2stage": ["conv_general.hip", "two_stage.hip", "ps_internal.h"],
     "convT_2stage": ["convt_softmax.hip", "two_stage.hip", "ps_internal.h"],
 }
@@ -101,8 +109,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (profiling runs)")
     ap.add_argument("--ops",
-                    default="conv,maxpool,convT,conv_bf16,conv_general,convT_bf16,conv_2stage,"
-                            "convT_2stage")
+                    default="conv,maxpool,convT,conv_bf16,conv_general,convT_bf16,maxpool_s2,"
+                            "maxpool_d2,conv_2stage,convT_2stage")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a 2 GiB device-to-device copy instead (counter calibration)")
     return ap.parse_args()
@@ -166,12 +174,19 @@ def main():
         runs["conv"] = lambda xd=xd, wd=wd, cb=cb, b2=b2, out=out: ps.conv_tanh_scale_bias_maxpool(
             xd, wd, cb, b2, 2.0, 4, out=out)
         del c
-    if "maxpool" in ops:
+    if any(o in ops for o in ("maxpool", "maxpool_s2", "maxpool_d2")):
         c = inputgen.workload("maxpool")
         xp = put(c["x"])
+        del c
+    if "maxpool" in ops:
         outp = torch.empty((32, 64, 511, 511), dtype=torch.float32, device=dev)
         runs["maxpool"] = lambda xp=xp, outp=outp: ps.maxpool2d(xp, 4, 1, 1, 1, out=outp)
-        del c
+    if "maxpool_s2" in ops:
+        outs2 = torch.empty((32, 64, 256, 256), dtype=torch.float32, device=dev)
+        runs["maxpool_s2"] = lambda xp=xp, outs2=outs2: ps.maxpool2d(xp, 3, 2, 1, 1, out=outs2)
+    if "maxpool_d2" in ops:
+        outd2 = torch.empty((32, 64, 512, 512), dtype=torch.float32, device=dev)
+        runs["maxpool_d2"] = lambda xp=xp, outd2=outd2: ps.maxpool2d(xp, 3, 1, 2, 2, out=outd2)
     if "convT" in ops:
         c = inputgen.workload("convT")
         xt, wt, cbt, b2t = put(c["x"]), put(c["w"]), put(c["convT_bias"]), put(c["bias2"])
@@ -310,6 +325,15 @@ def main():
                          "unit": "TFLOP/s", "frac": ach / PEAK_FP32,
                          "traffic": traffic("conv_general")}}
 
+    for name, nbytes in (("maxpool_s2", POOL_S2_BYTES), ("maxpool_d2", POOL_D2_BYTES)):
+        if name in runs:
+            mean, med, mn = stats(name)
+            ach = nbytes / (mean * 1e-3)
+            out_ops[name] = {
+                "value": ach / 1e9, "unit": "GB/s", "ms_mean": mean, "ms_median": med,
+                "ms_min": mn, "gbytes_per_launch": nbytes / 1e9,
+                "roofline": {"bound": "hbm", "achieved": ach / 1e9, "peak": PEAK_HBM / 1e9,
+                             "unit": "GB/s", "frac": ach / PEAK_HBM, "traffic": traffic(name)}}
     if "convT_bf16" in runs:
         mean, med, mn = stats("convT_bf16")
         bw = CONVT_BF16_BYTES / (mean * 1e-3)
@@ -377,6 +401,8 @@ def main():
             "conv_general_workload": "conv2d 64->128 k3 p1 + tanh + *2 + bias + maxpool k3 s2 p1, "
                                      "x fp32 [32,64,128,128] -> [32,128,64,64]",
             "convT_bf16_workload": "convT workload with bf16 x/w/out, fp32 accumulate",
+            "maxpool_s2_workload": "maxpool2d k3 s2 p1 on the maxpool input -> [32,64,256,256]",
+            "maxpool_d2_workload": "maxpool2d k3 s1 p2 d2 on the maxpool input -> [32,64,512,512]",
             "two_stage": "conv_2stage / convT_2stage: the conv and convT workloads unfused "
                          "(intermediate stored in HBM), for the fusion comparison",
         },

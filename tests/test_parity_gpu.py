@@ -66,6 +66,13 @@ POOL_CASES = [
     (1, 1, 17, 21, 3, 1, 1, 2),
     (1, 1, 1, 1, 2, 1, 1, 2),       # all-padding window -> -inf
     (1, 2, 12, 14, 4, 4, 0, 1),
+    (1, 2, 40, 50, 10, 3, 4, 1),    # window > 8: runtime-k kernel
+    (1, 1, 33, 70, 3, 2, 1, 2),     # stride 2 and dilation 2
+    (2, 3, 64, 64, 2, 2, 0, 1),
+    (1, 1, 20, 300, 5, 3, 2, 1),
+    (1, 2, 9, 9, 1, 1, 0, 1),       # k = 1: the identity
+    (1, 1, 30, 31, 16, 5, 8, 1),    # the largest window
+    (1, 70000, 4, 4, 2, 2, 0, 1),   # more planes than one grid dimension holds
 ]
 
 
@@ -98,6 +105,26 @@ def test_maxpool_full_workload(dev):
     got = out.cpu().numpy()
     del xd, out
     assert got.shape == (32, 64, 511, 511)
+    assert not np.isnan(got).any()
+    np.testing.assert_array_equal(got, ref)
+
+
+@pytest.mark.parametrize("k,st,p,d,shape", [(3, 2, 1, 1, (32, 64, 256, 256)),
+                                            (3, 1, 2, 2, (32, 64, 512, 512))])
+def test_maxpool_general_full_workload(dev, k, st, p, d, shape):
+    """The max-pool input under the downsampling (k3 s2 p1) and dilated (k3 s1 p2 d2)
+    windows the benchmark times, every output compared bit for bit."""
+    import pool_stencil_amd as ps
+    import torch
+    c = inputgen.workload("maxpool")
+    _say("maxpool general workload", (k, st, p, d))
+    ref = oracle.maxpool2d(c["x"], k, st, p, d)
+    assert ref.shape == shape
+    xd = _dev(c["x"], dev)
+    out = _canary(ref.shape, dev, torch.float32)
+    ps.maxpool2d(xd, k, st, p, d, out=out)
+    got = out.cpu().numpy()
+    del xd, out
     assert not np.isnan(got).any()
     np.testing.assert_array_equal(got, ref)
 
