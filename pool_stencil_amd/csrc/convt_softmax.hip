@@ -98,11 +98,13 @@ __global__ __launch_bounds__(kThreads) void convT_softmax_f32(
     const int64_t wstride = (int64_t)wg_per_class * (kThreads / 64);
     const float *aw = lw + j * CS + G * KS;  // + mt*16*CS + s
     const size_t plane = (size_t)H * W;
+    const uint32_t xbytes = 4u * (uint32_t)((size_t)N * Cin * plane);  // < 2^32 (host check)
+    const __amdgpu_buffer_rsrc_t xr = make_range_checked(x, xbytes);
     const size_t oplane = (size_t)OH * OW;
 
     for (int64_t tile = (int64_t)rank * (kThreads / 64) + wv; tile < ntiles; tile += wstride) {
         // per-lane pixel geometry for each of the NQ pixel groups
-        const float *xb[NQ];
+        uint32_t xb[NQ];   // byte offset of (n, G*Cq, ih0, iw0) in x
         bool r0[NQ], r1[NQ], c0[NQ], c1[NQ], pok[NQ];
         size_t obase[NQ];
 #pragma unroll
@@ -118,7 +120,7 @@ __global__ __launch_bounds__(kThreads) void convT_softmax_f32(
             r1[nq] = ih0 - 1 >= 0 && ih0 - 1 < H;
             c0[nq] = iw0 < W;
             c1[nq] = iw0 - 1 >= 0 && iw0 - 1 < W;
-            xb[nq] = x + ((size_t)n * Cin + (size_t)G * Cq) * plane + (size_t)ih0 * W + iw0;
+            xb[nq] = 4u * (uint32_t)(((size_t)n * Cin + (size_t)G * Cq) * plane + (size_t)ih0 * W + iw0);
             obase[nq] = (size_t)n * COUT * oplane + (size_t)(2 * m + a) * OW + (2 * q + b);
         }
 
@@ -129,17 +131,25 @@ __global__ __launch_bounds__(kThreads) void convT_softmax_f32(
             for (int nq = 0; nq < NQ; ++nq) acc[mt][nq] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
         // B operands of input channel cl of this lane group: the 2x2 input
-        // neighbourhood of each pixel, (u,v) = (0,0) (0,1) (1,0) (1,1)
+        // neighbourhood of each pixel, (u,v) = (0,0) (0,1) (1,0) (1,1).  Range-checked
+        // buffer loads: a tap outside the image (or a channel >= Cin) gets the offset
+        // xbytes, past the end of x, and reads zero.  The loads are unconditional, so
+        // the next channel's stay in flight while the current channel's MFMAs run
+        // (masked loads in branches made the compiler wait for all of them).
         auto load_b = [&](int cl, float (&bv)[NQ][4]) {
             const bool ciok = G * Cq + cl < Cin;
 #pragma unroll
             for (int nq = 0; nq < NQ; ++nq) {
-                const float *p = xb[nq] + (size_t)cl * plane;
+                const uint32_t o = xb[nq] + 4u * (uint32_t)cl * (uint32_t)plane;
                 const bool ok = ciok && pok[nq];
-                bv[nq][0] = (ok && r0[nq] && c0[nq]) ? p[0] : 0.f;
-                bv[nq][1] = (ok && r0[nq] && c1[nq]) ? p[-1] : 0.f;
-                bv[nq][2] = (ok && r1[nq] && c0[nq]) ? p[-W] : 0.f;
-                bv[nq][3] = (ok && r1[nq] && c1[nq]) ? p[-W - 1] : 0.f;
+                bv[nq][0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                    xr, (ok && r0[nq] && c0[nq]) ? o : xbytes, 0, 0));
+                bv[nq][1] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                    xr, (ok && r0[nq] && c1[nq]) ? o - 4u : xbytes, 0, 0));
+                bv[nq][2] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                    xr, (ok && r1[nq] && c0[nq]) ? o - 4u * (uint32_t)W : xbytes, 0, 0));
+                bv[nq][3] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                    xr, (ok && r1[nq] && c1[nq]) ? o - 4u * (uint32_t)(W + 1) : xbytes, 0, 0));
             }
         };
         auto compute = [&](int cl, const float (&bv)[NQ][4]) {
@@ -154,18 +164,20 @@ __global__ __launch_bounds__(kThreads) void convT_softmax_f32(
                                                                            acc[mt][nq], 0, 0, 0);
             }
         };
-        // two channels per trip: the next channel's loads are in flight while the
-        // current one feeds the matrix cores
-        float bA[NQ][4], bB[NQ][4];
+        // three channel buffers: the loads of the next two channels are in flight while
+        // the current one feeds the matrix cores.  Loads are unconditional (those past
+        // the last channel are unused), so the waits on them stay partial.
+        float bA[NQ][4], bB[NQ][4], bC[NQ][4];
         load_b(0, bA);
-        int cl = 0;
-        for (; cl + 1 < Cq; cl += 2) {
-            load_b(cl + 1, bB);
+        load_b(1, bB);
+        for (int cl = 0; cl < Cq; cl += 3) {
+            load_b(cl + 2, bC);
             compute(cl, bA);
-            if (cl + 2 < Cq) load_b(cl + 2, bA);
-            compute(cl + 1, bB);
+            load_b(cl + 3, bA);
+            if (cl + 1 < Cq) compute(cl + 1, bB);
+            load_b(cl + 4, bB);
+            if (cl + 2 < Cq) compute(cl + 2, bC);
         }
-        if (cl < Cq) compute(cl, bA);
 
         // ---- epilogue: D row 4G + r of tile mt = channel 16mt + 4G + r ----
         if constexpr (!SOFTMAX) {
@@ -230,6 +242,8 @@ int launch_mt(const float *x, const float *w, const float *cb, const float *b2, 
     const int KS = 4 * Cq;
     const size_t lds_bytes = ((size_t)16 * MT * (4 * KS + 4) + 2 * 16 * MT) * sizeof(float);
     if (lds_bytes > 160 * 1024) return PS_ERR_UNSUPPORTED;
+    // byte offsets into x are 32-bit (range-checked buffer loads)
+    if ((int64_t)N * Cin * H * W >= (1ll << 30)) return PS_ERR_UNSUPPORTED;
     int dev = 0, ncu = 0;
     if (hipGetDevice(&dev) != hipSuccess) return PS_ERR_HIP;
     if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)

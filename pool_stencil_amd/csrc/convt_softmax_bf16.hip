@@ -43,9 +43,7 @@ constexpr int ring_steps() { return MT >= 4 ? 2 : 4; }
 
 constexpr int kThreads = 512;  // 8 waves: two per SIMD
 constexpr float kLog2e = 1.4426950408889634f;
-// Fourth word of a raw buffer resource on gfx9-family GPUs (data format fields as the
-// ROCm libraries set them for untyped buffer access).
-constexpr int kBufferDword3 = 0x00020000;
+
 
 template <int MT>  // Cout = 32 * MT
 __global__ __launch_bounds__(kThreads, 1) void convT_softmax_bf16(
@@ -99,8 +97,7 @@ __global__ __launch_bounds__(kThreads, 1) void convT_softmax_bf16(
     // range-checked view of x (raw buffer, byte offsets; the host keeps its size
     // below 2^31 bytes)
     const uint32_t xbytes = 2u * (uint32_t)(N * Cin * plane);
-    const __amdgpu_buffer_rsrc_t xr =
-        __builtin_amdgcn_make_buffer_rsrc((void *)x, 0, (int)xbytes, kBufferDword3);
+    const __amdgpu_buffer_rsrc_t xr = make_range_checked(x, xbytes);
 
     for (int tile = rank * (kThreads / 64) + wv; tile < ntiles; tile += wstride) {
         // element offsets from the tensor bases (the host keeps N*Cin*H*W, N*Cout*OH*OW

@@ -60,6 +60,16 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
     return __uint_as_float((uint32_t)b << 16);
 }
 
+// Raw buffer resource over [base, base + bytes): loads through it are range-checked
+// by the hardware, and an offset at or past `bytes` reads as zero (used to express
+// zero padding without branches).  The fourth word is the gfx9-family setting for
+// untyped buffer access, as the ROCm libraries use it.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_range_checked(const void *base,
+                                                                     uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes,
+                                             0x00020000);
+}
+
 // Blocks of one launch are handed to the 8 XCDs of an MI355X round-robin
 // (block b runs on XCD b % 8).  This remaps the hardware block index so that
 // consecutive LOGICAL blocks (which share halo rows and weights) run on the
