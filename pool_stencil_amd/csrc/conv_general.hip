@@ -334,7 +334,7 @@ __global__ __launch_bounds__(kThreads, 2) void conv_general(
             float best = -INFINITY;
             for (int a = 0; a < g.pk; ++a)
                 for (int bb = 0; bb < g.pk; ++bb) best = fmaxf(best, yr[a * g.pd * g.CC + bb * g.pd]);
-            const float o = best == -INFINITY ? -INFINITY : tanhf(sgn * best) * g.scale + b2[co];
+            const float o = best == -INFINITY ? -INFINITY : tanh_exp(sgn * best) * g.scale + b2[co];
             store_out(y + (((size_t)n * g.Cout + co) * g.PH + ph) * g.PW + pw, o);
         }
     }

@@ -58,15 +58,6 @@ struct TileGeom {
     static constexpr int RS = PK * Q;        // entries per tile row
 };
 
-// tanh from the identity tanh(v) = 1 - 2 / (exp(2v) + 1), with the hardware
-// exponential and reciprocal.  Absolute error is about 1e-7 over the whole
-// range (exp overflow gives +1, underflow -1); used where the result is
-// rounded to bf16 (one bf16 ulp near 1 is 2^-8).
-__device__ __forceinline__ float tanh_exp(float v) {
-    const float e = __expf(2.f * v);
-    return 1.f - 2.f * __builtin_amdgcn_rcpf(e + 1.f);
-}
-
 // ---------------------------------------------------------------- fp32 ---
 // fp32 conv tuning: 16-byte halo loads issued per batch (bounds the registers the
 // fill holds next to the resident weights), window columns per unrolled group (0 =
@@ -255,7 +246,7 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? PS_CONV_MIN_WAVES : 1)) void c
                     if (co < Cout) {
                         const float v = sgn * best[nt][r] + s_bias[0][cl];
                         y[(((size_t)n * Cout + co) * PH + ph) * PW + pw] =
-                            tanhf(v) * scale + s_bias[1][cl];
+                            tanh_exp(v) * scale + s_bias[1][cl];
                     }
                 }
         }

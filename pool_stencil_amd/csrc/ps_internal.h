@@ -60,6 +60,16 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
     return __uint_as_float((uint32_t)b << 16);
 }
 
+// tanh from the identity tanh(v) = 1 - 2 / (exp(2v) + 1), with the hardware
+// exponential and reciprocal: about 10 instructions instead of the library
+// tanhf's 40.  Absolute error below 7e-7 over the whole range (checked in fp32
+// with exp and reciprocal perturbed by 2 ulp; exp overflow gives +1, underflow
+// -1), against the 1e-4 absolute bar of the fp32 outputs.
+__device__ __forceinline__ float tanh_exp(float v) {
+    const float e = __expf(2.f * v);
+    return 1.f - 2.f * __builtin_amdgcn_rcpf(e + 1.f);
+}
+
 // Raw buffer resource over [base, base + bytes): loads through it are range-checked
 // by the hardware, and an offset at or past `bytes` reads as zero (used to express
 // zero padding without branches).  The fourth word is the gfx9-family setting for

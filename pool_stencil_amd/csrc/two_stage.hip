@@ -53,7 +53,7 @@ __global__ __launch_bounds__(256) void tanh_scale_bias_maxpool_k(
                 best = fmaxf(best, sgn * ld(yp + (size_t)ih * W + iw));
             }
         }
-        const float o = best == -INFINITY ? -INFINITY : tanhf(sgn * best) * scale + b2[pl % C];
+        const float o = best == -INFINITY ? -INFINITY : tanh_exp(sgn * best) * scale + b2[pl % C];
         st(out + (size_t)pl * OH * OW + q, o);
     }
 }
