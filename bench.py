@@ -64,12 +64,14 @@ CONVT_BF16_BYTES = 128 * 64 * 64 * 64 * 2 + 128 * 128 * 129 * 129 * 2 + 64 * 128
 # x1.0.  `src` is the hash of the kernel's sources when the counters were taken; a
 # kernel edited since then reports traffic null.  See profiles/traffic_*.md.
 TRAFFIC = {
-    "conv": {"src": "ccea3519e3dc96f0", "fetch_bytes": 266854673, "write_bytes": 130644640},
-    "maxpool": {"src": "f44fd1c7e36e4898", "fetch_bytes": 2336400872, "write_bytes": 2140929824},
-    "convT": {"src": "4c7a01bc82e390b8", "fetch_bytes": 755485730, "write_bytes": 2825737152},
-    "conv_bf16": {"src": "ccea3519e3dc96f0", "fetch_bytes": 136757796, "write_bytes": 83142592},
-    "conv_general": {"src": "b71c9dcee23d6117", "fetch_bytes": 137186207, "write_bytes": 68958208},
-    "convT_bf16": {"src": "acf350b13cdc96cf", "fetch_bytes": 370533792, "write_bytes": 1275527744},
+    "conv": {"src": "8cee2fd820c40903", "fetch_bytes": 266782066, "write_bytes": 130621600},
+    "maxpool": {"src": "0bda7a9250dd91c0", "fetch_bytes": 2336415953, "write_bytes": 2141008864},
+    "maxpool_s2": {"src": "0bda7a9250dd91c0", "fetch_bytes": 3217028270, "write_bytes": 536870912},
+    "maxpool_d2": {"src": "0bda7a9250dd91c0", "fetch_bytes": 3605004257, "write_bytes": 2147483648},
+    "convT": {"src": "63055175720cdbf2", "fetch_bytes": 841453583, "write_bytes": 2733284640},
+    "conv_bf16": {"src": "8cee2fd820c40903", "fetch_bytes": 136745491, "write_bytes": 83098080},
+    "conv_general": {"src": "0eb52815cce67b91", "fetch_bytes": 137199630, "write_bytes": 69029952},
+    "convT_bf16": {"src": "609e3b338e8e1f1f", "fetch_bytes": 371189356, "write_bytes": 1274985152},
 }
 KERNEL_SOURCES = {
     "conv": ["conv_pool.hip", "ps_internal.h"],

@@ -25,9 +25,12 @@
 //   - patch: [ci][row][col], channel stride padded to 16 (mod 64) words, so
 //     the four lane groups of a wave (one input channel each) use disjoint
 //     banks;
-//   - weights: [tap][ci][co] with channel co = 16*cb + c at word 4*c + cb of
-//     its 64-word row, so one 16-byte LDS read gives a lane the A operands of
-//     all four 16-channel blocks.
+//   - weights: one 68-word row per k = ci*T + tap of the chunk, channel
+//     co = 16*cb + c at word 4*c + cb, so one 16-byte LDS read gives a lane the
+//     A operands of all four 16-channel blocks (and the fill's writes, 16
+//     consecutive k of 4 channels per instruction, hit distinct banks).
+// When a chunk's fill fits in registers, the next chunk's loads are issued
+// before the current chunk's MFMA work and written to LDS after it.
 //
 // Epilogue (fused): the region is written to LDS as sgn*(y) (sgn = -1 when
 // scale < 0) with -inf where the pool's padding lies, each thread takes the
