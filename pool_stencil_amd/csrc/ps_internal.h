@@ -48,12 +48,10 @@ int launch_tanh_scale_bias_maxpool(const void *y, const float *bias2, void *out,
 int launch_softmax_bias_scale_sigmoid(const float *y, const float *bias2, float *out, int N,
                                       int C, int H, int W, float scale, hipStream_t stream);
 
-// fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN).
+// fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN): the hardware
+// conversion (v_cvt_pk_bf16_f32 on gfx950), one instruction per pair of values.
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
