@@ -260,7 +260,7 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? PS_CONV_MIN_WAVES : 1)) void c
 // 8 bf16): pooled row ph reads ring rows PK*ph - pad ... + PK + 1, while the PK
 // rows that pooled row ph+1 adds are loaded from HBM into registers during the
 // MFMA work of row ph and written to the ring afterwards.  One barrier per row.
-template <int PK, int NPW, bool VEC>
+template <int PK, int NPW, bool VEC, bool MULTI>
 __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? 2 : 1)) void conv_pool_bf16(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, const float *__restrict__ cb,
     const float *__restrict__ b2, uint16_t *__restrict__ y, int Cin, int H, int W, int Cout,
@@ -360,11 +360,14 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? 2 : 1)) void conv_pool_bf16(
             }
         }
     };
+    // Epilogue constants: with u = sgn*best + cb, tanh(u) = 1 - 2/(2^(2u log2e) + 1), so
+    // out = (scale + b2) - 2 scale / (2^(best*k2 + cb*2log2e) + 1), k2 = 2 log2e sgn.
+    constexpr float kTwoLog2e = 2.8853900817779268f;
     auto stage_bias = [&](int ct) {
         if (threadIdx.x < 64) {
             const int co = ct + threadIdx.x;
-            s_bias[0][threadIdx.x] = (co < Cout && cb) ? cb[co] : 0.f;
-            s_bias[1][threadIdx.x] = co < Cout ? b2[co] : 0.f;
+            s_bias[0][threadIdx.x] = (co < Cout && cb) ? cb[co] * kTwoLog2e : 0.f;
+            s_bias[1][threadIdx.x] = co < Cout ? scale + b2[co] : 0.f;
         }
     };
 
@@ -400,9 +403,19 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? 2 : 1)) void conv_pool_bf16(
         }
     }
     const int pw = pwt * G::T + 16 * wv + j;
-    const float sgn = scale < 0.f ? -1.f : 1.f;
-    const bool single_tile = Cout <= 64;
-    if (single_tile) {
+    const float k2 = scale < 0.f ? -kTwoLog2e : kTwoLog2e;
+    const float m2 = -2.f * scale;
+    // Output stores go through a range-checked resource over image n's Cout planes:
+    // a store at or past its end is dropped, which masks channels >= Cout without
+    // branches; columns pw >= PW take an offset far past the end (the host keeps
+    // (Cout + 64) planes under 2^31 bytes, so no offset wraps).
+    const uint32_t cplane = (uint32_t)(PH * PW);
+    const __amdgpu_buffer_rsrc_t yr =
+        make_range_checked(y + (size_t)n * Cout * cplane, 2u * (uint32_t)Cout * cplane);
+    const uint32_t lane_off = pw < PW ? 2u * ((uint32_t)(4 * g4) * cplane + (uint32_t)pw) : 0x80000000u;
+    // MULTI: Cout > 64, the weights and biases of each 64-channel tile are reloaded per row
+    constexpr bool single_tile = !MULTI;
+    if constexpr (single_tile) {
         load_weights(0);
         stage_bias(0);
     }
@@ -425,7 +438,7 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? 2 : 1)) void conv_pool_bf16(
 
         const int rbase = PK * ph - pad;
         for (int ct = 0; ct < Cout; ct += 64) {
-            if (!single_tile) {
+            if constexpr (!single_tile) {
                 __syncthreads();
                 load_weights(ct);
                 stage_bias(ct);
@@ -457,25 +470,36 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? 2 : 1)) void conv_pool_bf16(
                         for (int r = 0; r < 4; ++r) best[nt][r] = fmaxf(best[nt][r], acc[nt][r]);
                 }
             }
-            if (pw < PW) {
-                // output (n, co, ph, pw): the lane's first channel, then constant strides
-                const size_t cplane = (size_t)PH * PW;
-                uint16_t *yrow = y + ((size_t)n * Cout + ct + 4 * g4) * cplane + (size_t)ph * PW + pw;
+            // One channel tile: write the prefetched rows to the ring before the output
+            // stores (their ring slots are not read by row ph), so that waiting for the
+            // loads does not also wait for the output stores (on this chip a wait on a
+            // load issued before pending stores waits for those stores too).
+            if (single_tile && more) {
 #pragma unroll
-                for (int nt = 0; nt < 4; ++nt)
+                for (int i = 0; i < NPER; ++i) {
+                    const int e = threadIdx.x + i * NT;
+                    if (e < NTOT) store_group(nr0 + e / NG, e % NG, pre[i]);
+                }
+            }
+            // output (n, co = ct + 16 nt + 4 g4 + r, ph, pw)
+            const uint32_t row_off = lane_off + 2u * ((uint32_t)ct * cplane + (uint32_t)(ph * PW));
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int cl = 16 * nt + 4 * g4 + r;
-                        if (ct + cl < Cout) {
-                            const float v = sgn * best[nt][r] + s_bias[0][cl];
-                            yrow[(size_t)(16 * nt + r) * cplane] =
-                                f32_to_bf16_rne(tanh_exp(v) * scale + s_bias[1][cl]);
-                        }
-                    }
+            for (int nt = 0; nt < 4; ++nt) {
+                const float4 cbv = *(const float4 *)&s_bias[0][16 * nt + 4 * g4];
+                const float4 c2v = *(const float4 *)&s_bias[1][16 * nt + 4 * g4];
+                const float cbr[4] = {cbv.x, cbv.y, cbv.z, cbv.w};
+                const float c2r[4] = {c2v.x, c2v.y, c2v.z, c2v.w};
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float e = __builtin_amdgcn_exp2f(fmaf(best[nt][r], k2, cbr[r]));
+                    const float o = fmaf(m2, __builtin_amdgcn_rcpf(e + 1.f), c2r[r]);
+                    __builtin_amdgcn_raw_buffer_store_b16(
+                        f32_to_bf16_rne(o), yr, (int)(row_off + 2u * (uint32_t)(16 * nt + r) * cplane),
+                        0, 0);
+                }
             }
         }
-
-        if (more) {
+        if (!single_tile && more) {
 #pragma unroll
             for (int i = 0; i < NPER; ++i) {
                 const int e = threadIdx.x + i * NT;
@@ -505,16 +529,17 @@ int launch_pk_npw(const void *x, const void *w, const float *cb, const float *b2
         if (nblocks > 0x7fffffffull) return PS_ERR_UNSUPPORTED;
         // every strip starts at a multiple of 16*NPW*PK columns, so alignment is uniform
         const bool vec = (pad % 8 == 0) && (W % 8 == 0);
-        if (vec)
-            hipLaunchKernelGGL((conv_pool_bf16<PK, NPW, true>), dim3((unsigned)nblocks),
-                               dim3(64 * NPW), 0, stream, (const uint16_t *)x, (const uint16_t *)w,
-                               cb, b2, (uint16_t *)y, Cin, H, W, Cout, pad, PH, PW, scale, npwt,
-                               (int)nseg);
-        else
-            hipLaunchKernelGGL((conv_pool_bf16<PK, NPW, false>), dim3((unsigned)nblocks),
-                               dim3(64 * NPW), 0, stream, (const uint16_t *)x, (const uint16_t *)w,
-                               cb, b2, (uint16_t *)y, Cin, H, W, Cout, pad, PH, PW, scale, npwt,
-                               (int)nseg);
+        const bool multi = Cout > 64;
+        const dim3 grid((unsigned)nblocks), block(64 * NPW);
+#define PS_BF16_LAUNCH(V, M)                                                                  \
+    hipLaunchKernelGGL((conv_pool_bf16<PK, NPW, V, M>), grid, block, 0, stream,                \
+                       (const uint16_t *)x, (const uint16_t *)w, cb, b2, (uint16_t *)y, Cin, H, W, \
+                       Cout, pad, PH, PW, scale, npwt, (int)nseg)
+        if (vec && !multi) PS_BF16_LAUNCH(true, false);
+        else if (vec) PS_BF16_LAUNCH(true, true);
+        else if (!multi) PS_BF16_LAUNCH(false, false);
+        else PS_BF16_LAUNCH(false, true);
+#undef PS_BF16_LAUNCH
         return hipGetLastError() == hipSuccess ? PS_OK : PS_ERR_HIP;
     }
     const uint64_t nblocks = (uint64_t)N * PH * npwt;
