@@ -234,6 +234,223 @@ __global__ __launch_bounds__(kThreads, 1) void convT_softmax_bf16(
     }
 }
 
+// ---------------------------------------------------------------------------------
+// Staged variant, taken when W % 8 == 0 and its buffers fit the LDS.
+//
+// Indexing the pixels of a row class by input position instead: output (oh, ow) =
+// (2r - a, 2c - b) takes input rows r - u and columns c - v (u, v in {0, 1}) with
+// kernel taps kh = 1 - a + 2u, kw = 1 - b + 2v, so the B operand of position (r, c)
+// is the same for both column classes b and one B fragment feeds the MFMAs of both
+// (positions c = 0 .. W cover every output column; ow outside [0, OW) is masked).
+//
+// Input channels are staged 8 at a time in LDS, channel-last: [slot][col + 1][8
+// channels], 16 bytes per entry, with zero entries at columns -1 and W, so a lane's B
+// fragment (8 channels of one tap) is one 16-byte LDS read.  The global reads that
+// fill a chunk are 16 bytes wide (8 columns of one channel) and are issued one chunk
+// ahead; a thread transposes two channels x 8 columns with byte permutes into 8
+// 4-byte LDS writes.  K order: k = 32*(ci/8) + 8*(2u + v) + ci%8; K-step s = (chunk
+// ci/8, u), lane half h holding tap v = h.
+//
+// Work item: 256 consecutive positions p = m*(W + 1) + c of one image and row class
+// (8 waves x 32), which touch at most `slots` input rows.
+constexpr int kStagedPix = 256;
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+template <int MT>  // Cout = 32 * MT
+__global__ __launch_bounds__(kThreads, 1) void convT_softmax_bf16_staged(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
+    const float *__restrict__ cbias, const float *__restrict__ b2, uint16_t *__restrict__ y,
+    int N, int Cin, int H, int W, int OH, int OW, float scale, int C8, int slots,
+    int wg_per_class) {
+    constexpr int COUT = 32 * MT;
+    extern __shared__ float lds[];
+    const int K = 4 * C8;
+    const int KP = K + 8;                         // bf16 per weight row (16-byte pad)
+    uint16_t *la = (uint16_t *)lds;               // [b][COUT][KP]
+    float *lcb = lds + COUT * KP;                 // conv-transpose bias * log2e
+    float *lb2 = lcb + COUT;                      // -bias2 * scale * log2e
+    uint4 *lx = (uint4 *)(lb2 + COUT);            // [2][slots][W + 2] input entries
+    const int WE = W + 2;
+    const int bufsz = slots * WE;
+
+    const int blk = blockIdx.x;
+    const int a = (blk >> 3) & 1;
+    const int rank = (blk & 7) + 8 * (blk >> 4);
+    const int Mc = (OH - a + 1) >> 1;             // rows r = m + a of this row class
+    const int Wc = W + 1;                         // positions c = 0 .. W
+    const int npix = Mc * Wc;
+    const int ipi = (npix + kStagedPix - 1) / kStagedPix;  // items per image
+    const int nitems = N * ipi;
+    if (rank >= nitems) return;                   // whole block: before any barrier
+
+    for (int e = threadIdx.x; e < 2 * COUT * K; e += kThreads) {
+        const int k = e % K;
+        const int rest = e / K;
+        const int co = rest % COUT, b = rest / COUT;
+        const int ci = 8 * (k >> 5) + (k & 7);
+        const int t = (k >> 3) & 3;
+        const int kh = 1 - a + 2 * (t >> 1), kw = 1 - b + 2 * (t & 1);
+        la[(b * COUT + co) * KP + k] = ci < Cin ? w[(((size_t)ci * COUT + co) * 4 + kh) * 4 + kw] : 0;
+    }
+    for (int e = threadIdx.x; e < COUT; e += kThreads) {
+        lcb[e] = (cbias ? cbias[e] : 0.f) * kLog2e;
+        lb2[e] = -b2[e] * scale * kLog2e;
+    }
+    for (int e = threadIdx.x; e < 2 * slots; e += kThreads) {
+        lx[e * WE] = make_uint4(0u, 0u, 0u, 0u);
+        lx[e * WE + W + 1] = make_uint4(0u, 0u, 0u, 0u);
+    }
+
+    // ---- chunk fill: thread -> (slot, 8-column group g, channel pair cp) ----
+    const int W8 = W >> 3;
+    const int f_cp = threadIdx.x & 3;
+    const int f_g = (threadIdx.x >> 2) % W8;
+    const int f_slot = (threadIdx.x >> 2) / W8;
+    const bool f_on = f_slot < slots;
+    const uint32_t plane = (uint32_t)(H * W);
+    const uint32_t xbytes = 2u * (uint32_t)(N * Cin) * plane;
+    const __amdgpu_buffer_rsrc_t xr = make_range_checked(x, xbytes);
+    auto fill_load = [&](int it, int k, uint32_t (&v)[8]) {
+        const int n = it / ipi;
+        const int m0 = ((it - n * ipi) * kStagedPix) / Wc;
+        const int ir = m0 + a - 1 + f_slot;
+        const int ch = 8 * k + 2 * f_cp;
+        const bool rok = f_on && ir >= 0 && ir < H;
+        const uint32_t o = 2u * (((uint32_t)(n * Cin + ch) * (uint32_t)H + (uint32_t)ir) * (uint32_t)W +
+                                 8u * (uint32_t)f_g);
+        const u32x4 v0 = __builtin_amdgcn_raw_buffer_load_b128(xr, (rok && ch < Cin) ? o : xbytes, 0, 0);
+        const u32x4 v1 = __builtin_amdgcn_raw_buffer_load_b128(
+            xr, (rok && ch + 1 < Cin) ? o + 2u * plane : xbytes, 0, 0);
+        v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w;
+        v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
+    };
+    auto fill_store = [&](int buf, const uint32_t (&v)[8]) {
+        if (f_on) {
+            uint32_t *dst = (uint32_t *)(lx + buf * bufsz + f_slot * WE + 8 * f_g + 1) + f_cp;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                dst[4 * e] = __builtin_amdgcn_perm(v[4 + (e >> 1)], v[e >> 1],
+                                                   (e & 1) ? 0x07060302u : 0x05040100u);
+        }
+    };
+
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+    const int j = lane & 31;  // position (B/D column) and A row within a 32-channel tile
+    const int h = lane >> 5;  // K half of a step (tap v = h); D row half
+    const int nchunks = C8 / 8;
+    const int oplane = OH * OW;
+    const float ninv_s = -scale * kLog2e;
+    const uint32_t ybytes = 2u * (uint32_t)COUT * (uint32_t)oplane;
+
+    uint32_t pre[8];
+    int it = rank;
+    fill_load(it, 0, pre);
+    fill_store(0, pre);
+    __syncthreads();
+    int buf = 0;
+
+    for (; it < nitems; it += wg_per_class) {
+        const int n = it / ipi;
+        const int p0 = (it - n * ipi) * kStagedPix;
+        const int m0 = p0 / Wc;
+        const int p = p0 + 32 * wv + j;
+        const bool pv = p < npix;
+        const int pc = pv ? p : p0;
+        const int m = pc / Wc;
+        const int c = pc - m * Wc;
+        // B entries of taps (u, v = h), u = 0, 1: input (m + a - u, c - h)
+        const int eo0 = (m - m0 + 1) * WE + (c - h + 1);
+        const int eo1 = eo0 - WE;
+        const uint16_t *ab = la + j * KP + 8 * h;
+
+        f32x16 acc[2][MT];
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[b][mt][i] = 0.f;
+
+        for (int k = 0; k < nchunks; ++k) {
+            const bool last = k + 1 == nchunks;
+            const bool more = !last || it + wg_per_class < nitems;
+            if (more) fill_load(last ? it + wg_per_class : it, last ? 0 : k + 1, pre);
+            const uint4 *xb = lx + buf * bufsz;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const bf16x8 bop = __builtin_bit_cast(bf16x8, xb[u ? eo1 : eo0]);
+                const int s = 2 * k + u;
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) {
+                        const uint4 av = *(const uint4 *)(ab + (b * COUT + 32 * mt) * KP + 16 * s);
+                        acc[b][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            __builtin_bit_cast(bf16x8, av), bop, acc[b][mt], 0, 0, 0);
+                    }
+            }
+            if (more) fill_store(buf ^ 1, pre);
+            __syncthreads();
+            buf ^= 1;
+        }
+
+        // ---- epilogue per column class: D element i of tile mt = channel
+        // 32mt + 8(i/4) + 4h + i%4; the partner lane (xor 32) holds the other half ----
+        const __amdgpu_buffer_rsrc_t yr =
+            make_range_checked(y + (size_t)n * COUT * oplane, ybytes);
+        const int oh = 2 * m + a;
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int i4 = 0; i4 < 4; ++i4) {
+                    const float4 cb4 = *(const float4 *)(lcb + 32 * mt + 8 * i4 + 4 * h);
+                    const float cbv[4] = {cb4.x, cb4.y, cb4.z, cb4.w};
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int i = 4 * i4 + r;
+                        acc[b][mt][i] = fmaf(acc[b][mt][i], kLog2e, cbv[r]);
+                        mx = fmaxf(mx, acc[b][mt][i]);
+                    }
+                }
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            float sum = 0.f;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    acc[b][mt][i] = __builtin_amdgcn_exp2f(acc[b][mt][i] - mx);
+                    sum += acc[b][mt][i];
+                }
+            sum += __shfl_xor(sum, 32);
+            const float inv = ninv_s * __builtin_amdgcn_rcpf(sum);
+            // a masked store gets an offset past the end of the range (dropped)
+            const int ow = 2 * c - b;
+            const bool ok = pv && ow >= 0 && ow < OW;
+            const uint32_t yo = ok ? 2u * (uint32_t)(4 * h * oplane + oh * OW + ow) : 0x80000000u;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int i4 = 0; i4 < 4; ++i4) {
+                    const int co0 = 32 * mt + 8 * i4;
+                    const float4 b4 = *(const float4 *)(lb2 + co0 + 4 * h);
+                    const float bv[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float t = __builtin_amdgcn_exp2f(fmaf(acc[b][mt][4 * i4 + r], inv, bv[r]));
+                        __builtin_amdgcn_raw_buffer_store_b16(
+                            f32_to_bf16_rne(__builtin_amdgcn_rcpf(1.f + t)), yr,
+                            (int)(yo + 2u * (uint32_t)(co0 + r) * (uint32_t)oplane), 0, 0);
+                    }
+                }
+        }
+    }
+}
+
 template <int MT>
 int launch_mt(const uint16_t *x, const uint16_t *w, const float *cb, const float *b2, uint16_t *y,
               int N, int Cin, int H, int W, int OH, int OW, float scale, hipStream_t stream) {
@@ -253,6 +470,29 @@ int launch_mt(const uint16_t *x, const uint16_t *w, const float *cb, const float
     int wg_per_class = (ncu + 1) / 2;
     wg_per_class = ((wg_per_class + 7) / 8) * 8;
     const int nblocks = 2 * wg_per_class;
+
+    // staged variant: 16-byte input rows, every fill unit one thread, buffers in LDS,
+    // and masked output offsets (2^31 + image bytes) that cannot wrap
+    {
+        const int C8 = (Cin + 7) / 8 * 8;
+        const int Wc = W + 1;
+        const int slots = (Wc + kStagedPix - 2) / Wc + 2;
+        const size_t lds_staged = (size_t)2 * 32 * MT * (4 * C8 + 8) * 2 +
+                                  2 * 32 * MT * sizeof(float) + (size_t)2 * slots * (W + 2) * 16;
+        if (W % 8 == 0 && (int64_t)slots * (W / 8) * 4 <= kThreads &&
+            lds_staged <= 160 * 1024 && (int64_t)2 * 32 * MT * OH * OW < (1ll << 31)) {
+            if (lds_staged > 65536 &&
+                hipFuncSetAttribute((const void *)convT_softmax_bf16_staged<MT>,
+                                    hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    (int)lds_staged) != hipSuccess)
+                return PS_ERR_HIP;
+            hipLaunchKernelGGL((convT_softmax_bf16_staged<MT>), dim3(nblocks), dim3(kThreads),
+                               lds_staged, stream, x, w, cb, b2, y, N, Cin, H, W, OH, OW, scale,
+                               C8, slots, wg_per_class);
+            return hipGetLastError() == hipSuccess ? PS_OK : PS_ERR_HIP;
+        }
+    }
+
     if (lds_bytes > 65536 &&
         hipFuncSetAttribute((const void *)convT_softmax_bf16<MT>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes) !=

@@ -269,6 +269,14 @@ CONVT_BF16_CASES = [
     dict(N=2, Cin=64, H=8, W=8, Cout=128, scale=-0.5, convT_bias=False),
     dict(N=1, Cin=32, H=12, W=20, Cout=96),
     dict(N=1, Cin=70, H=6, W=70, Cout=128),       # Cin not a multiple of 4; 3 column blocks
+    # W a multiple of 8: the LDS-staged kernel (the 16- and 8-wide cases above too)
+    dict(N=2, Cin=13, H=5, W=8, Cout=32),         # one ragged channel chunk
+    dict(N=1, Cin=20, H=7, W=16, Cout=96, output_padding=0),
+    dict(N=3, Cin=64, H=9, W=24, Cout=128),       # items end mid-row, three images
+    dict(N=1, Cin=8, H=1, W=8, Cout=64),          # one input row
+    dict(N=2, Cin=64, H=4, W=64, Cout=128, scale=-0.5),
+    dict(N=1, Cin=32, H=3, W=160, Cout=64),       # rows longer than a work item
+    dict(N=1, Cin=16, H=2, W=256, Cout=32, output_padding=0),
 ]
 
 
