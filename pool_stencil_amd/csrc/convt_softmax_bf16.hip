@@ -254,6 +254,7 @@ __global__ __launch_bounds__(kThreads, 1) void convT_softmax_bf16(
 // Work item: 256 consecutive positions p = m*(W + 1) + c of one image and row class
 // (8 waves x 32), which touch at most `slots` input rows.
 constexpr int kStagedPix = 256;
+constexpr int kStageRow = 66;  // bf16 per row of a wave's output staging (64 + pad)
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
@@ -273,6 +274,8 @@ __global__ __launch_bounds__(kThreads, 1) void convT_softmax_bf16_staged(
     uint4 *lx = (uint4 *)(lb2 + COUT);            // [2][slots][W + 2] input entries
     const int WE = W + 2;
     const int bufsz = slots * WE;
+    // per wave: 8 channels x 64 output columns of bf16 outputs on their way to memory
+    uint16_t *lo = (uint16_t *)(lx + 2 * bufsz) + (threadIdx.x >> 6) * 8 * kStageRow;
 
     const int blk = blockIdx.x;
     const int a = (blk >> 3) & 1;
@@ -396,11 +399,9 @@ __global__ __launch_bounds__(kThreads, 1) void convT_softmax_bf16_staged(
             buf ^= 1;
         }
 
-        // ---- epilogue per column class: D element i of tile mt = channel
-        // 32mt + 8(i/4) + 4h + i%4; the partner lane (xor 32) holds the other half ----
-        const __amdgpu_buffer_rsrc_t yr =
-            make_range_checked(y + (size_t)n * COUT * oplane, ybytes);
-        const int oh = 2 * m + a;
+        // ---- epilogue: D element i of tile mt = channel 32mt + 8(i/4) + 4h + i%4; the
+        // partner lane (xor 32) holds the other half of each 8-channel group ----
+        float inv[2];
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
             float mx = -INFINITY;
@@ -427,27 +428,45 @@ __global__ __launch_bounds__(kThreads, 1) void convT_softmax_bf16_staged(
                     sum += acc[b][mt][i];
                 }
             sum += __shfl_xor(sum, 32);
-            const float inv = ninv_s * __builtin_amdgcn_rcpf(sum);
-            // a masked store gets an offset past the end of the range (dropped)
-            const int ow = 2 * c - b;
-            const bool ok = pv && ow >= 0 && ow < OW;
-            const uint32_t yo = ok ? 2u * (uint32_t)(4 * h * oplane + oh * OW + ow) : 0x80000000u;
+            inv[b] = ninv_s * __builtin_amdgcn_rcpf(sum);
+        }
+        // The 32 positions x 2 column classes of the wave are 64 output columns
+        // ow = 2c - b, ascending within an output row: slot 2j + 1 - b.  Each 8-channel
+        // group goes through LDS so that a store writes one channel's 64 columns (128
+        // contiguous bytes, or two runs where the positions wrap to the next row).
+        // Store lane L takes slot L: position L/2, class 1 - L%2; a masked store gets
+        // an offset past the end of the range (dropped).
+        const __amdgpu_buffer_rsrc_t yr =
+            make_range_checked(y + (size_t)n * COUT * oplane, ybytes);
+        const int ps = p0 + 32 * wv + (lane >> 1);
+        const bool psv = ps < npix;
+        const int msx = psv ? ps / Wc : 0;
+        const int ows = 2 * (psv ? ps - msx * Wc : 0) - (1 - (lane & 1));
+        const uint32_t so = (psv && ows >= 0 && ows < OW)
+                                ? 2u * (uint32_t)((2 * msx + a) * OW + ows)
+                                : 0x80000000u;
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                for (int i4 = 0; i4 < 4; ++i4) {
-                    const int co0 = 32 * mt + 8 * i4;
-                    const float4 b4 = *(const float4 *)(lb2 + co0 + 4 * h);
-                    const float bv[4] = {b4.x, b4.y, b4.z, b4.w};
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const int co0 = 32 * mt + 8 * i4;
+                const float4 b4 = *(const float4 *)(lb2 + co0 + 4 * h);
+                const float bv[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const float t = __builtin_amdgcn_exp2f(fmaf(acc[b][mt][4 * i4 + r], inv, bv[r]));
-                        __builtin_amdgcn_raw_buffer_store_b16(
-                            f32_to_bf16_rne(__builtin_amdgcn_rcpf(1.f + t)), yr,
-                            (int)(yo + 2u * (uint32_t)(co0 + r) * (uint32_t)oplane), 0, 0);
+                        const float t =
+                            __builtin_amdgcn_exp2f(fmaf(acc[b][mt][4 * i4 + r], inv[b], bv[r]));
+                        lo[(4 * h + r) * kStageRow + 2 * j + 1 - b] =
+                            f32_to_bf16_rne(__builtin_amdgcn_rcpf(1.f + t));
                     }
-                }
-        }
+#pragma unroll
+                for (int ch = 0; ch < 8; ++ch)
+                    __builtin_amdgcn_raw_buffer_store_b16(
+                        lo[ch * kStageRow + lane], yr,
+                        (int)(so + 2u * (uint32_t)(co0 + ch) * (uint32_t)oplane), 0, 0);
+            }
     }
 }
 
@@ -478,7 +497,8 @@ int launch_mt(const uint16_t *x, const uint16_t *w, const float *cb, const float
         const int Wc = W + 1;
         const int slots = (Wc + kStagedPix - 2) / Wc + 2;
         const size_t lds_staged = (size_t)2 * 32 * MT * (4 * C8 + 8) * 2 +
-                                  2 * 32 * MT * sizeof(float) + (size_t)2 * slots * (W + 2) * 16;
+                                  2 * 32 * MT * sizeof(float) + (size_t)2 * slots * (W + 2) * 16 +
+                                  (size_t)(kThreads / 64) * 8 * kStageRow * 2;
         if (W % 8 == 0 && (int64_t)slots * (W / 8) * 4 <= kThreads &&
             lds_staged <= 160 * 1024 && (int64_t)2 * 32 * MT * OH * OW < (1ll << 31)) {
             if (lds_staged > 65536 &&
