@@ -64,14 +64,14 @@ CONVT_BF16_BYTES = 128 * 64 * 64 * 64 * 2 + 128 * 128 * 129 * 129 * 2 + 64 * 128
 # x1.0.  `src` is the hash of the kernel's sources when the counters were taken; a
 # kernel edited since then reports traffic null.  See profiles/traffic_*.md.
 TRAFFIC = {
-    "conv": {"src": "8cee2fd820c40903", "fetch_bytes": 266782066, "write_bytes": 130621600},
-    "maxpool": {"src": "0bda7a9250dd91c0", "fetch_bytes": 2336415953, "write_bytes": 2141008864},
-    "maxpool_s2": {"src": "0bda7a9250dd91c0", "fetch_bytes": 3217028270, "write_bytes": 536870912},
-    "maxpool_d2": {"src": "0bda7a9250dd91c0", "fetch_bytes": 3605004257, "write_bytes": 2147483648},
-    "convT": {"src": "63055175720cdbf2", "fetch_bytes": 841453583, "write_bytes": 2733284640},
-    "conv_bf16": {"src": "8cee2fd820c40903", "fetch_bytes": 136745491, "write_bytes": 83098080},
-    "conv_general": {"src": "0eb52815cce67b91", "fetch_bytes": 137199630, "write_bytes": 69029952},
-    "convT_bf16": {"src": "609e3b338e8e1f1f", "fetch_bytes": 371189356, "write_bytes": 1274985152},
+    "conv": {"src": "1ec6295bccaac937", "fetch_bytes": 266756677, "write_bytes": 130617712},
+    "conv_bf16": {"src": "1ec6295bccaac937", "fetch_bytes": 136677080, "write_bytes": 83661552},
+    "maxpool": {"src": "74fbba42c00fac8a", "fetch_bytes": 2336366475, "write_bytes": 2140982480},
+    "maxpool_s2": {"src": "74fbba42c00fac8a", "fetch_bytes": 3216960585, "write_bytes": 536870912},
+    "maxpool_d2": {"src": "74fbba42c00fac8a", "fetch_bytes": 3604926552, "write_bytes": 2147483648},
+    "convT": {"src": "f657ef3944880ea9", "fetch_bytes": 833696287, "write_bytes": 2734077648},
+    "convT_bf16": {"src": "c35853eab2c487e4", "fetch_bytes": 119830774, "write_bytes": 589944064},
+    "conv_general": {"src": "0e26e00736bf879f", "fetch_bytes": 137200392, "write_bytes": 68993632},
 }
 KERNEL_SOURCES = {
     "conv": ["conv_pool.hip", "ps_internal.h"],
