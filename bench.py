@@ -66,9 +66,9 @@ CONVT_BF16_BYTES = 128 * 64 * 64 * 64 * 2 + 128 * 128 * 129 * 129 * 2 + 64 * 128
 TRAFFIC = {
     "conv": {"src": "1ec6295bccaac937", "fetch_bytes": 266756677, "write_bytes": 130617712},
     "conv_bf16": {"src": "1ec6295bccaac937", "fetch_bytes": 136677080, "write_bytes": 83661552},
-    "maxpool": {"src": "74fbba42c00fac8a", "fetch_bytes": 2336366475, "write_bytes": 2140982480},
-    "maxpool_s2": {"src": "74fbba42c00fac8a", "fetch_bytes": 3216960585, "write_bytes": 536870912},
-    "maxpool_d2": {"src": "74fbba42c00fac8a", "fetch_bytes": 3604926552, "write_bytes": 2147483648},
+    "maxpool": {"src": "7e1bb71d82108743", "fetch_bytes": 2160257829, "write_bytes": 2140686592},
+    "maxpool_s2": {"src": "7e1bb71d82108743", "fetch_bytes": 3216960585, "write_bytes": 536870912},
+    "maxpool_d2": {"src": "7e1bb71d82108743", "fetch_bytes": 3604917593, "write_bytes": 2147483648},
     "convT": {"src": "f657ef3944880ea9", "fetch_bytes": 833696287, "write_bytes": 2734077648},
     "convT_bf16": {"src": "c35853eab2c487e4", "fetch_bytes": 119830774, "write_bytes": 589944064},
     "conv_general": {"src": "0e26e00736bf879f", "fetch_bytes": 137200392, "write_bytes": 68993632},

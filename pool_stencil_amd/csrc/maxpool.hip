@@ -22,9 +22,11 @@
 //                        (the separable max of the l1_p42 page, done in
 //                        registers rather than through a shared-memory tile);
 //                      - each output row is written as V coalesced wave stores.
-//                    The band's k-1 halo rows are the only re-reads; four
-//                    consecutive bands of a plane share a workgroup, so the
-//                    halo is served by L1/L2.
+//                    The k-1 input rows shared by neighbouring bands are read
+//                    from HBM once: eight consecutive bands of a plane share a
+//                    workgroup, and each wave hands the horizontal maxima of
+//                    its band's first k-1 rows to the wave of the band above
+//                    through LDS (only every eighth band boundary re-reads).
 //   maxpool_cols     any k, stride, pad, dilation: a thread owns one output
 //                    column of 8 (stride 1) or 1 consecutive output rows; every
 //                    window tap is a branch-free load (see the kernel).
@@ -52,11 +54,17 @@ constexpr int kWave = 64;
 #define PS_MAXPOOL_NT_LOAD 0
 #endif
 // Resident workgroups per CU (0 = as many as registers allow).  Fewer concurrent
-// row streams keep more DRAM pages open per stream: on MI355X three workgroups
-// (12 waves) per CU moved the k4 s1 p1 pool from 4.9 to 5.2 TB/s.  The cap is
-// applied by reserving a matching share of the CU's LDS for each workgroup.
+// row streams keep more DRAM pages open per stream.  The cap is applied by
+// reserving a matching share of the CU's LDS for each workgroup.
 #ifndef PS_MAXPOOL_WGS_PER_CU
-#define PS_MAXPOOL_WGS_PER_CU 3
+#define PS_MAXPOOL_WGS_PER_CU 1
+#endif
+// Waves (consecutive bands of one plane) per workgroup: all but the last hand their
+// halo rows over through LDS.  Measured on MI355X (k4 s1 p1, 32x64x512x512): one
+// 8-wave workgroup per CU beats 4 waves at 3 per CU by about 3%, and 16 resident
+// waves per CU (either shape) is 8-10% slower than 8.
+#ifndef PS_MAXPOOL_WG_WAVES
+#define PS_MAXPOOL_WG_WAVES 8
 #endif
 
 __device__ __forceinline__ float rot_lanes(float v, int src_lane_x4) {
@@ -83,14 +91,22 @@ __device__ __forceinline__ void widen(float (&v)[V + 1], int lane, int shift) {
 }
 
 template <int K, int V, int PF>
-__global__ __launch_bounds__(256) void maxpool_s1_rows(
+__global__ __launch_bounds__(kWave * PS_MAXPOOL_WG_WAVES) void maxpool_s1_rows(
     const float *__restrict__ x, float *__restrict__ y, int H, int W, int OH, int OW, int pad,
     int band_rows, int nbands, int nstrips, uint64_t ntasks) {
+    // [wave][K-1][V][64]: the horizontal maxima of each band's first K-1 input rows,
+    // which are also the last K-1 input rows of the band above it
+    extern __shared__ float halo[];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x >> 6;
+    const int nw = blockDim.x >> 6;
     const uint32_t blk = xcd_remap(blockIdx.x, gridDim.x);
-    const uint64_t task = (uint64_t)blk * (blockDim.x >> 6) + wave;
-    if (task >= ntasks) return;
+    const uint64_t task = (uint64_t)blk * nw + wave;
+    // Every wave passes the kernel's one barrier exactly once, idle waves included.
+    if (task >= ntasks) {
+        __syncthreads();
+        return;
+    }
     const int band = (int)(task % (uint64_t)nbands);
     const uint64_t t2 = task / (uint64_t)nbands;
     const int strip = (int)(t2 % (uint64_t)nstrips);
@@ -104,6 +120,13 @@ __global__ __launch_bounds__(256) void maxpool_s1_rows(
     const int oh1 = min(OH, oh0 + band_rows);
     const int ih_first = oh0 - pad;
     const int ih_last = oh1 - 1 - pad + K - 1;
+    const int nrows = ih_last - ih_first + 1;
+    // The next wave of the workgroup holds the band below in the same plane and strip
+    // (task + 1): its first K-1 input rows are this band's last K-1, so their
+    // horizontal maxima come from the LDS instead of a second HBM read.  Such a band
+    // is not the plane's last, so it has band_rows >= K - 1 rows of its own to load.
+    const bool from_below = wave + 1 < nw && band + 1 < nbands;
+    const int nload = nrows - (from_below ? K - 1 : 0);  // >= K - 1
 
     // Column validity is fixed for the whole band.
     bool colok[V + 1];
@@ -125,27 +148,55 @@ __global__ __launch_bounds__(256) void maxpool_s1_rows(
 #endif
     };
 
+    // Append input row r's horizontal maxima to the vertical ring of the last K and,
+    // once K rows are in, write output row r - (K-1) of the band.
+    float ring[K][V];
+    auto consume = [&](int r, const float (&v)[V + 1]) {
+#pragma unroll
+        for (int i = 0; i < K - 1; ++i)
+#pragma unroll
+            for (int j = 0; j < V; ++j) ring[i][j] = ring[i + 1][j];
+#pragma unroll
+        for (int j = 0; j < V; ++j) ring[K - 1][j] = v[j];
+
+        if (r >= K - 1) {
+            const int oh = oh0 + r - (K - 1);
+            float *orow = yp + (int64_t)oh * OW + c0 + lane;
+#pragma unroll
+            for (int j = 0; j < V; ++j) {
+                float m = ring[0][j];
+#pragma unroll
+                for (int i = 1; i < K; ++i) m = fmax_ordered(m, ring[i][j]);
+                if (c0 + kWave * j + lane < OW) {
+#if PS_MAXPOOL_NT_STORE
+                    __builtin_nontemporal_store(m, orow + kWave * j);
+#else
+                    orow[kWave * j] = m;
+#endif
+                }
+            }
+        }
+    };
+
     // PF input rows are in flight at any time: slot s of `pf` holds row
     // ih_first + base + s; after a row is consumed its slot is refilled with the
     // row PF further down.  The slot loop is unrolled, so every register index is
     // static and no pending load is ever copied.
-    const int nrows = ih_last - ih_first + 1;
     float pf[PF][V + 1];
 #pragma unroll
     for (int s = 0; s < PF; ++s)
-        if (s < nrows) load_row(ih_first + s, pf[s]);
+        if (s < nload) load_row(ih_first + s, pf[s]);
 
-    float ring[K][V];
-    for (int base = 0; base < nrows; base += PF) {
+    for (int base = 0; base < nload; base += PF) {
 #pragma unroll
         for (int s = 0; s < PF; ++s) {
             const int r = base + s;
-            if (r >= nrows) break;
+            if (r >= nload) break;
             const int ih = ih_first + r;
             float v[V + 1];
 #pragma unroll
             for (int j = 0; j <= V; ++j) v[j] = pf[s][j];
-            if (r + PF < nrows) load_row(ih + PF, pf[s]);
+            if (r + PF < nload) load_row(ih + PF, pf[s]);
 
             // horizontal window-K max by doubling: window 1 -> 2 -> 4 (-> 8)
             constexpr int P = K >= 8 ? 8 : K >= 4 ? 4 : K >= 2 ? 2 : 1;  // largest power of 2 <= K
@@ -164,31 +215,21 @@ __global__ __launch_bounds__(256) void maxpool_s1_rows(
                 for (int j = 0; j < V; ++j) v[j] = fmax_ordered(v[j], carry ? rot[j + 1] : rot[j]);
             }
 
-            // shift the vertical ring and append this row's horizontal maxima
+            // hand the first K-1 rows to the band above (the previous wave)
+            if (r < K - 1 && wave > 0) {
 #pragma unroll
-            for (int i = 0; i < K - 1; ++i)
-#pragma unroll
-                for (int j = 0; j < V; ++j) ring[i][j] = ring[i + 1][j];
-#pragma unroll
-            for (int j = 0; j < V; ++j) ring[K - 1][j] = v[j];
-
-            if (r >= K - 1) {
-                const int oh = ih - (K - 1) + pad;
-                float *orow = yp + (int64_t)oh * OW + c0 + lane;
-#pragma unroll
-                for (int j = 0; j < V; ++j) {
-                    float m = ring[0][j];
-#pragma unroll
-                    for (int i = 1; i < K; ++i) m = fmax_ordered(m, ring[i][j]);
-                    if (c0 + kWave * j + lane < OW) {
-#if PS_MAXPOOL_NT_STORE
-                        __builtin_nontemporal_store(m, orow + kWave * j);
-#else
-                        orow[kWave * j] = m;
-#endif
-                    }
-                }
+                for (int j = 0; j < V; ++j) halo[((wave * (K - 1) + r) * V + j) * kWave + lane] = v[j];
             }
+            if (r == K - 2) __syncthreads();
+            consume(r, v);
+        }
+    }
+    if (from_below) {
+        for (int i = 0; i < K - 1; ++i) {
+            float v[V + 1];
+#pragma unroll
+            for (int j = 0; j < V; ++j) v[j] = halo[(((wave + 1) * (K - 1) + i) * V + j) * kWave + lane];
+            consume(nload + i, v);
         }
     }
 }
@@ -279,7 +320,7 @@ int occupancy_cap_lds_bytes() {
         hipSuccess)
         return 0;
     const int share = lds / PS_MAXPOOL_WGS_PER_CU - 256;
-    return share > 0 && share <= 65536 ? share : 0;
+    return share > 0 ? share : 0;
 }
 
 template <int K, int V>
@@ -289,10 +330,19 @@ int launch_rows(const float *x, float *y, int N, int C, int H, int W, int OH, in
     const int nbands = (OH + band_rows - 1) / band_rows;
     const int nstrips = (OW + kWave * V - 1) / (kWave * V);
     const uint64_t ntasks = (uint64_t)N * C * nstrips * nbands;
-    const uint64_t nblocks = (ntasks + 3) / 4;
+    constexpr int nw = PS_MAXPOOL_WG_WAVES;
+    const uint64_t nblocks = (ntasks + nw - 1) / nw;
     if (nblocks > 0x7fffffffull) return PS_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL((maxpool_s1_rows<K, V, PS_MAXPOOL_PREFETCH>), dim3((unsigned)nblocks), dim3(256),
-                       occupancy_cap_lds_bytes(), stream,
+    // the halo hand-over buffer, at least the occupancy cap's LDS share
+    const int halo_bytes = nw * (K - 1) * V * kWave * (int)sizeof(float);
+    const int cap_bytes = occupancy_cap_lds_bytes();
+    const int lds_bytes = cap_bytes > halo_bytes ? cap_bytes : halo_bytes;
+    if (lds_bytes > 65536 &&
+        hipFuncSetAttribute((const void *)maxpool_s1_rows<K, V, PS_MAXPOOL_PREFETCH>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes) != hipSuccess)
+        return PS_ERR_HIP;
+    hipLaunchKernelGGL((maxpool_s1_rows<K, V, PS_MAXPOOL_PREFETCH>), dim3((unsigned)nblocks), dim3(kWave * nw),
+                       lds_bytes, stream,
                        x, y, H, W, OH, OW, p, band_rows, nbands, nstrips, ntasks);
     return hipGetLastError() == hipSuccess ? PS_OK : PS_ERR_HIP;
 }

@@ -61,6 +61,11 @@ POOL_CASES = [
     (1, 1, 40, 200, 7, 1, 3, 1),
     (1, 1, 19, 90, 8, 1, 0, 1),
     (1, 1, 5, 5, 4, 1, 3, 1),       # windows at the border only touch padding partly
+    # bands of 32 output rows: the band below hands its first k-1 rows over through LDS
+    (1, 3, 160, 96, 4, 1, 1, 1),    # 5 bands a plane: planes straddle workgroups
+    (2, 1, 300, 70, 8, 1, 7, 1),    # k 8 with the largest padding, 10 bands
+    (1, 5, 128, 40, 2, 1, 1, 1),    # k 2, a 1-row last band
+    (1, 2, 97, 257, 6, 1, 5, 1),    # two strips, k 6
     (2, 2, 31, 29, 2, 2, 0, 1),     # direct kernel from here on
     (1, 2, 25, 27, 3, 2, 1, 1),
     (1, 1, 17, 21, 3, 1, 1, 2),
