@@ -69,7 +69,7 @@ TRAFFIC = {
     "maxpool": {"src": "7e1bb71d82108743", "fetch_bytes": 2160257829, "write_bytes": 2140686592},
     "maxpool_s2": {"src": "7e1bb71d82108743", "fetch_bytes": 3216960585, "write_bytes": 536870912},
     "maxpool_d2": {"src": "7e1bb71d82108743", "fetch_bytes": 3604917593, "write_bytes": 2147483648},
-    "convT": {"src": "f657ef3944880ea9", "fetch_bytes": 833696287, "write_bytes": 2734077648},
+    "convT": {"src": "bc73f067020da62b", "fetch_bytes": 593611393, "write_bytes": 2352869296},
     "convT_bf16": {"src": "c35853eab2c487e4", "fetch_bytes": 119830774, "write_bytes": 589944064},
     "conv_general": {"src": "0e26e00736bf879f", "fetch_bytes": 137200392, "write_bytes": 68993632},
 }

@@ -252,6 +252,8 @@ CONVT_CASES = [
     dict(N=1, Cin=1, H=1, W=1, Cout=16),
     dict(N=2, Cin=64, H=8, W=8, Cout=128, scale=-0.5, convT_bias=False),
     dict(N=1, Cin=32, H=12, W=20, Cout=112),
+    dict(N=1, Cin=70, H=6, W=70, Cout=128),       # Cin not a multiple of 4, 150 KB of weights
+    dict(N=4, Cin=7, H=13, W=9, Cout=64, output_padding=0),  # channels past Cin, last image
 ]
 
 
