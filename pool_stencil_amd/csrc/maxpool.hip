@@ -5,7 +5,7 @@
 //   y[n,c,oh,ow] = max_{kh,kw<k} x[n,c, oh*s - p + kh*d, ow*s - p + kw*d],
 //   positions outside the image count as -inf, floor mode.
 //
-// Two kernels:
+// Three kernels:
 //   maxpool_s1_rows  stride 1, dilation 1, window k <= 8, pad < k.  The case
 //                    that is pure HBM streaming (every input is read about once,
 //                    every output written once).  One wavefront owns a band of
@@ -27,6 +27,9 @@
 //                    workgroup, and each wave hands the horizontal maxima of
 //                    its band's first k-1 rows to the wave of the band above
 //                    through LDS (only every eighth band boundary re-reads).
+//   maxpool_rows_sd  k 2..5 with stride / dilation (2,1), (3,1), (1,2), (2,2): the
+//                    same row streaming, each input row staged in the wave's LDS
+//                    buffer and its strided / dilated taps read back from there.
 //   maxpool_cols     any k, stride, pad, dilation: a thread owns one output
 //                    column of 8 (stride 1) or 1 consecutive output rows; every
 //                    window tap is a branch-free load (see the kernel).
@@ -58,6 +61,32 @@ constexpr int kWave = 64;
 // reserving a matching share of the CU's LDS for each workgroup.
 #ifndef PS_MAXPOOL_WGS_PER_CU
 #define PS_MAXPOOL_WGS_PER_CU 1
+#endif
+// Strided / dilated streaming kernel: output columns per strip (64*V), output rows
+// per band at stride 1 and at stride >= 2, rows of loads in flight, resident
+// workgroups per CU at stride 1 and at stride >= 2 (0 = as many as registers allow).
+// Measured on MI355X over the 32x64x512x512 input: k3 s2 p1 0.546 ms with 32-row
+// bands and no cap, 0.470 ms with 8-row bands and 2 workgroups per CU (4-row
+// bands, 1 or 3 per CU slower); k3 s1 p2 d2 0.875 ms with 64-row bands, 0.773 ms
+// with 16-row bands and 4 per CU (8 or 12 rows, 2, 3 or 6 per CU slower); V = 8
+// and 3 prefetched rows slower.
+#ifndef PS_MPSD_V
+#define PS_MPSD_V 4
+#endif
+#ifndef PS_MPSD_BAND_S1
+#define PS_MPSD_BAND_S1 16
+#endif
+#ifndef PS_MPSD_BAND_S2
+#define PS_MPSD_BAND_S2 8
+#endif
+#ifndef PS_MPSD_PF
+#define PS_MPSD_PF 2
+#endif
+#ifndef PS_MPSD_WGS_S1
+#define PS_MPSD_WGS_S1 4
+#endif
+#ifndef PS_MPSD_WGS_S2
+#define PS_MPSD_WGS_S2 2
 #endif
 // Waves (consecutive bands of one plane) per workgroup: all but the last hand their
 // halo rows over through LDS.  Measured on MI355X (k4 s1 p1, 32x64x512x512): one
@@ -234,6 +263,146 @@ __global__ __launch_bounds__(kWave * PS_MAXPOOL_WG_WAVES) void maxpool_s1_rows(
     }
 }
 
+// Strided and dilated windows (compile-time K, S, D), streamed by rows like
+// maxpool_s1_rows: one wavefront owns a band of output rows of one (n,c) plane and a
+// strip of 64*V output columns, and reads each input row of its band once:
+//   - the row's span of input columns (64*V*S + (K-1)*D of them) is loaded as
+//     coalesced 256-byte wave loads (-inf outside the image) and written to the
+//     wave's own LDS row buffer;
+//   - lane l's horizontal window max for output column 64j + l is read back from
+//     LDS at the K fixed addresses (64j + l)*S + kw*D;
+//   - a register ring keeps the horizontal maxima of the last (K-1)*D + 1 input
+//     rows; whenever an input row completes output row oh (row oh*S - p + (K-1)*D),
+//     the vertical max over the ring's taps 0, D, .., (K-1)*D is written.
+// Neighbouring bands share (K-1)*D + 1 - S input rows, which both read.
+template <int K, int S, int D, int V, int PF>
+__global__ __launch_bounds__(256) void maxpool_rows_sd(
+    const float *__restrict__ x, float *__restrict__ y, int H, int W, int OH, int OW, int pad,
+    int band_rows, int nbands, int nstrips, uint64_t ntasks) {
+    constexpr int R = (K - 1) * D + 1;                        // input rows per window
+    constexpr int SPAN = (kWave * V - 1) * S + (K - 1) * D + 1;  // input columns per strip
+    constexpr int NCH = (SPAN + kWave - 1) / kWave;           // 64-column load chunks
+    __shared__ float lrow[4][NCH * kWave];                    // one row buffer per wave
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x >> 6;
+    const uint32_t blk = xcd_remap(blockIdx.x, gridDim.x);
+    const uint64_t task = (uint64_t)blk * 4 + wave;
+    if (task >= ntasks) return;
+    const int band = (int)(task % (uint64_t)nbands);
+    const uint64_t t2 = task / (uint64_t)nbands;
+    const int strip = (int)(t2 % (uint64_t)nstrips);
+    const uint64_t plane = t2 / (uint64_t)nstrips;
+
+    const float *xp = x + plane * (uint64_t)H * W;
+    float *yp = y + plane * (uint64_t)OH * OW;
+    const int c0 = strip * (kWave * V);  // first output column of the strip
+    const int ic0 = c0 * S - pad;        // input column of buffer entry 0
+    const int oh0 = band * band_rows;
+    const int oh1 = min(OH, oh0 + band_rows);
+    const int ih_first = oh0 * S - pad;
+    const int nrows = (oh1 - 1 - oh0) * S + R;  // input rows of the band
+    float *buf = lrow[wave];
+
+    bool colok[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int ic = ic0 + kWave * c + lane;
+        colok[c] = ic >= 0 && ic < W;
+    }
+    auto load_row = [&](int ih, float (&v)[NCH]) {
+        const bool rowok = ih >= 0 && ih < H;
+        const float *rp = xp + (int64_t)ih * W + ic0 + lane;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) v[c] = (rowok && colok[c]) ? rp[kWave * c] : -INFINITY;
+    };
+
+    float pf[PF][NCH];
+#pragma unroll
+    for (int s = 0; s < PF; ++s)
+        if (s < nrows) load_row(ih_first + s, pf[s]);
+
+    float ring[R][V];
+    for (int base = 0; base < nrows; base += PF) {
+#pragma unroll
+        for (int s = 0; s < PF; ++s) {
+            const int r = base + s;
+            if (r >= nrows) break;
+            // the row into the wave's LDS buffer, the slot refilled PF rows further down
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) buf[kWave * c + lane] = pf[s][c];
+            if (r + PF < nrows) load_row(ih_first + r + PF, pf[s]);
+            __builtin_amdgcn_wave_barrier();
+            float hm[V];
+#pragma unroll
+            for (int j = 0; j < V; ++j) {
+                const float *bp = buf + (kWave * j + lane) * S;
+                float m = bp[0];
+#pragma unroll
+                for (int kw = 1; kw < K; ++kw) m = fmax_ordered(m, bp[kw * D]);
+                hm[j] = m;
+            }
+            __builtin_amdgcn_wave_barrier();  // the next row's writes come after these reads
+#pragma unroll
+            for (int i = 0; i < R - 1; ++i)
+#pragma unroll
+                for (int j = 0; j < V; ++j) ring[i][j] = ring[i + 1][j];
+#pragma unroll
+            for (int j = 0; j < V; ++j) ring[R - 1][j] = hm[j];
+            const int q = r - (R - 1);  // = (oh - oh0) * S when row r completes output oh
+            if (q >= 0 && q % S == 0) {
+                const int oh = oh0 + q / S;
+                float *orow = yp + (int64_t)oh * OW + c0 + lane;
+#pragma unroll
+                for (int j = 0; j < V; ++j) {
+                    float m = ring[0][j];
+#pragma unroll
+                    for (int kh = 1; kh < K; ++kh) m = fmax_ordered(m, ring[kh * D][j]);
+                    if (c0 + kWave * j + lane < OW) orow[kWave * j] = m;
+                }
+            }
+        }
+    }
+}
+
+int occupancy_cap_lds_bytes(int wgs);
+
+template <int K, int S, int D>
+int launch_rows_sd(const float *x, float *y, int N, int C, int H, int W, int OH, int OW, int p,
+                   hipStream_t stream) {
+    constexpr int V = PS_MPSD_V;
+    const int band_rows = S >= 2 ? PS_MPSD_BAND_S2 : PS_MPSD_BAND_S1;
+    const int nbands = (OH + band_rows - 1) / band_rows;
+    const int nstrips = (OW + kWave * V - 1) / (kWave * V);
+    const uint64_t ntasks = (uint64_t)N * C * nstrips * nbands;
+    const uint64_t nblocks = (ntasks + 3) / 4;
+    if (nblocks > 0x7fffffffull) return PS_ERR_UNSUPPORTED;
+    const int lds_bytes = occupancy_cap_lds_bytes(S >= 2 ? PS_MPSD_WGS_S2 : PS_MPSD_WGS_S1);
+    if (lds_bytes > 65536 &&
+        hipFuncSetAttribute((const void *)maxpool_rows_sd<K, S, D, V, PS_MPSD_PF>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes) != hipSuccess)
+        return PS_ERR_HIP;
+    hipLaunchKernelGGL((maxpool_rows_sd<K, S, D, V, PS_MPSD_PF>), dim3((unsigned)nblocks),
+                       dim3(256), lds_bytes, stream, x, y, H, W, OH, OW, p, band_rows, nbands,
+                       nstrips, ntasks);
+    return hipGetLastError() == hipSuccess ? PS_OK : PS_ERR_HIP;
+}
+
+// (K, S, D) combinations with a streaming kernel; -1 when there is none.
+int launch_rows_sd_any(const float *x, float *y, int N, int C, int H, int W, int OH, int OW,
+                       int k, int s, int p, int d, hipStream_t stream) {
+#define PS_SD(KK, SS, DD)                                                               \
+    if (k == KK && s == SS && d == DD)                                                  \
+        return launch_rows_sd<KK, SS, DD>(x, y, N, C, H, W, OH, OW, p, stream);
+#define PS_SD_K(SS, DD) PS_SD(2, SS, DD) PS_SD(3, SS, DD) PS_SD(4, SS, DD) PS_SD(5, SS, DD)
+    PS_SD_K(2, 1)
+    PS_SD_K(3, 1)
+    PS_SD_K(1, 2)
+    PS_SD_K(2, 2)
+#undef PS_SD_K
+#undef PS_SD
+    return -1;
+}
+
 // Any window, stride, padding and dilation.  A thread owns one output column ow of
 // RB consecutive output rows of one plane; the lanes of a wave take consecutive
 // columns, so a window tap's load is a coalesced row read (s = 1) or a row read
@@ -311,15 +480,15 @@ __global__ __launch_bounds__(256) void maxpool_cols(const float *__restrict__ x,
     }
 }
 
-// Dynamic LDS bytes that leave room for exactly PS_MAXPOOL_WGS_PER_CU workgroups per CU.
-int occupancy_cap_lds_bytes() {
-    if (PS_MAXPOOL_WGS_PER_CU <= 0) return 0;
+// Dynamic LDS bytes that leave room for exactly `wgs` workgroups per CU (0: no cap).
+int occupancy_cap_lds_bytes(int wgs) {
+    if (wgs <= 0) return 0;
     int dev = 0, lds = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
         hipSuccess)
         return 0;
-    const int share = lds / PS_MAXPOOL_WGS_PER_CU - 256;
+    const int share = lds / wgs - 12 * 1024;  // below the share, static LDS included
     return share > 0 ? share : 0;
 }
 
@@ -335,7 +504,7 @@ int launch_rows(const float *x, float *y, int N, int C, int H, int W, int OH, in
     if (nblocks > 0x7fffffffull) return PS_ERR_UNSUPPORTED;
     // the halo hand-over buffer, at least the occupancy cap's LDS share
     const int halo_bytes = nw * (K - 1) * V * kWave * (int)sizeof(float);
-    const int cap_bytes = occupancy_cap_lds_bytes();
+    const int cap_bytes = occupancy_cap_lds_bytes(PS_MAXPOOL_WGS_PER_CU);
     const int lds_bytes = cap_bytes > halo_bytes ? cap_bytes : halo_bytes;
     if (lds_bytes > 65536 &&
         hipFuncSetAttribute((const void *)maxpool_s1_rows<K, V, PS_MAXPOOL_PREFETCH>,
@@ -371,6 +540,10 @@ int launch_maxpool2d(const float *x, float *y, int N, int C, int H, int W, int O
             case 7: return launch_rows_k<7>(x, y, N, C, H, W, OH, OW, p, stream);
             case 8: return launch_rows_k<8>(x, y, N, C, H, W, OH, OW, p, stream);
         }
+    }
+    {
+        const int rc = launch_rows_sd_any(x, y, N, C, H, W, OH, OW, k, s, p, d, stream);
+        if (rc >= 0) return rc;
     }
     // output rows per thread: 8 at stride 1 (neighbouring rows share most input rows
     // in the cache), 1 otherwise (MI355X: k3 s1 d2 1.20 ms at 8 vs 1.73 ms at 1;

@@ -78,6 +78,12 @@ POOL_CASES = [
     (1, 2, 9, 9, 1, 1, 0, 1),       # k = 1: the identity
     (1, 1, 30, 31, 16, 5, 8, 1),    # the largest window
     (1, 70000, 4, 4, 2, 2, 0, 1),   # more planes than one grid dimension holds
+    # strided / dilated row-streaming kernel: several bands and strips
+    (1, 2, 150, 600, 3, 2, 1, 1),   # k3 s2: 3 bands of 32 rows, 2 strips
+    (1, 3, 140, 100, 3, 1, 2, 2),   # k3 s1 d2: 3 bands of 64 rows
+    (2, 1, 70, 70, 4, 3, 3, 1),     # k4 s3, the largest padding
+    (1, 1, 200, 40, 5, 2, 4, 2),    # k5 s2 d2: 4 bands
+    (3, 2, 66, 520, 2, 1, 1, 2),    # k2 s1 d2: 3 strips, a ragged last strip
 ]
 
 
