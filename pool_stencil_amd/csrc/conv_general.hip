@@ -71,14 +71,22 @@ struct GenGeom {
 };
 
 // floor(n / d) for 0 <= n, n * d < 2^32, with m = ceil(2^32 / d) (m = 0 encodes d = 1).
+// Branch-free: with m = 0 the high product is 0 and n passes through the mask.
 __device__ __forceinline__ int fdiv(int n, uint32_t m) {
-    return m ? (int)__umulhi((uint32_t)n, m) : n;
+    const uint32_t keep = 0u - (uint32_t)(m == 0u);
+    return (int)(__umulhi((uint32_t)n, m) + ((uint32_t)n & keep));
 }
 
 constexpr int kWRS = 68;        // LDS words per weight row (64 channels + 4: conflict-free fill)
 
-__device__ __forceinline__ float to_f32(float v) { return v; }
-__device__ __forceinline__ float to_f32(uint16_t v) { return bf16_to_f32(v); }
+// Range-checked element loads: an offset at or past the resource's end reads zero.
+__device__ __forceinline__ float load_elem(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, const float *) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
+}
+__device__ __forceinline__ float load_elem(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, const uint16_t *) {
+    return bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, byte_off, 0, 0));
+}
+constexpr uint32_t kMaskedOff = 0x80000000u;  // past the end of every tensor here
 __device__ __forceinline__ void store_out(float *p, float v) { *p = v; }
 __device__ __forceinline__ void store_out(uint16_t *p, float v) { *p = f32_to_bf16_rne(v); }
 
@@ -132,11 +140,17 @@ __global__ __launch_bounds__(kThreads, 2) void conv_general(
 
     float *xs = smem;                    // [CK][PSZ]
     float *ws = smem + g.CK * g.PSZ;     // [CK*T][kWRS]: row k = ci*T + tap of the chunk
-    // Loads use 32-bit element offsets from workgroup-uniform bases (the host keeps
-    // one image and the weight tensor below 2^31 elements), so each in-flight load
-    // holds one VGPR of address.
+    // Loads are range-checked buffer loads with 32-bit byte offsets from
+    // workgroup-uniform bases (the host keeps one image and the weight tensor below
+    // 2^31 bytes), so each in-flight load holds one VGPR of address, and a value
+    // outside the image (the conv's zero padding) or past the weights is an
+    // unconditional load at a masked offset that reads zero: no branches.
     const TI *xn = x + (size_t)n * g.Cin * g.H * g.W;
     const uint32_t plane = (uint32_t)g.H * (uint32_t)g.W;
+    constexpr uint32_t esz = sizeof(TI);
+    const __amdgpu_buffer_rsrc_t xr = make_range_checked(xn, esz * (uint32_t)g.Cin * plane);
+    const __amdgpu_buffer_rsrc_t wrs =
+        make_range_checked(w, esz * (uint32_t)g.Cout * (uint32_t)g.Cin * (uint32_t)(g.kH * g.kW));
     const int ckt = g.CK * T;
     // Patch fill: the rows (ci, r) of a chunk are cut into segments of SW columns
     // (SW a power of two <= 64); one wave instruction covers 64/SW segments, lane ->
@@ -176,25 +190,26 @@ __global__ __launch_bounds__(kThreads, 2) void conv_general(
 #pragma unroll
         for (int j = 0; j < kMaxPR; ++j) {
             const int s = (wvu + 4 * (p * kMaxPR + j)) * spi + sb;
-            float v = 0.f;
-            if (s < nseg) {
-                const int row = fdiv(s, g.mCPL);
-                const int col = (s - row * g.CPL) * g.SW + scol;
-                const int ci = fdiv(row, g.mIR);
-                const int ih = ih0 + row - ci * g.IR, iw = iw0 + col;
-                if (col < g.IC && c0 + ci < g.Cin && ih >= 0 && ih < g.H && iw >= 0 && iw < g.W)
-                    v = to_f32(xn[(uint32_t)(c0 + ci) * plane + (uint32_t)(ih * g.W + iw)]);
-            }
-            pr[j] = v;
+            const int row = fdiv(s < nseg ? s : 0, g.mCPL);
+            const int col = ((s < nseg ? s : 0) - row * g.CPL) * g.SW + scol;
+            const int ci = fdiv(row, g.mIR);
+            const int ih = ih0 + row - ci * g.IR, iw = iw0 + col;
+            // (bitwise: a short-circuit chain compiles to a branch per load)
+            const bool ok = (s < nseg) & (col < g.IC) & (c0 + ci < g.Cin) & (ih >= 0) &
+                            (ih < g.H) & (iw >= 0) & (iw < g.W);
+            const uint32_t o = esz * ((uint32_t)(c0 + ci) * plane + (uint32_t)(ih * g.W + iw));
+            pr[j] = load_elem(xr, ok ? o : kMaskedOff, x);
         }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int co = ct + wvu + 4 * q + 16 * wcb;
-            const TI *wq = w + (uint32_t)(co < g.Cout ? co : 0) * wcs + (uint32_t)(c0 * T + wkk);
+            const uint32_t wq = esz * ((uint32_t)co * wcs + (uint32_t)(c0 * T + wkk));
 #pragma unroll
             for (int kb = 0; kb < kKB; ++kb) {
                 const int k = 16 * (p * kKB + kb) + wkk;
-                wr[q * kKB + kb] = (co < g.Cout && k < kvalid) ? to_f32(wq[16 * (p * kKB + kb)]) : 0.f;
+                const bool ok = (co < g.Cout) & (k < kvalid);
+                wr[q * kKB + kb] =
+                    load_elem(wrs, ok ? wq + esz * (uint32_t)(16 * (p * kKB + kb)) : kMaskedOff, w);
             }
         }
     };
@@ -462,7 +477,10 @@ int launch_conv_general(const void *x, const void *w, const float *conv_bias, co
         g.pk = pk; g.ps = ps_; g.pp = pp; g.pd = pd; g.PH = PH; g.PW = PW; g.scale = scale;
     }
     g.co_tiles = (Cout + kCoTile - 1) / kCoTile;
-    if ((int64_t)Cin * H * W >= (1ll << 31) || (int64_t)Cout * Cin * kH * kW >= (1ll << 31))
+    // 32-bit byte offsets with a masked offset of 2^31: one image and the weights
+    // below 2^31 bytes
+    const int64_t esz = dtype == PS_BF16 ? 2 : 4;
+    if ((int64_t)Cin * H * W * esz >= (1ll << 31) || (int64_t)Cout * Cin * kH * kW * esz >= (1ll << 31))
         return PS_ERR_UNSUPPORTED;
     int lds = 0;
     if (!plan(g, epi, lds)) return PS_ERR_UNSUPPORTED;
