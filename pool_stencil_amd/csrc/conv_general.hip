@@ -234,11 +234,78 @@ __global__ __launch_bounds__(kThreads, 2) void conv_general(
             }
     };
 
-    if constexpr (PF) load(0, 0);
+    // One-pass fill (PF): the lane's patch segments decode the same way for every
+    // chunk, so the decode runs once.  xoff: byte offset of the value in the chunk's
+    // first channel frame (masked outside the image); lidx: its LDS word, two 16-bit
+    // indices per register, or a per-lane dummy word after the weights when the value
+    // has no place.  Per chunk only scalar state changes: the resources start at
+    // channel c0 (input) and tap row c0*T (weights).  Channels past Cin then read zero
+    // (past the image's resource), and weight rows past Cin meet those zero patches.
+    uint32_t xoff[PF ? kMaxPR : 1], lidx[PF ? (kMaxPR + 1) / 2 : 1], woff[4];
+    const int dummy = g.CK * g.PSZ + ckt * kWRS + lane;
+    if constexpr (PF) {
+#pragma unroll
+        for (int j = 0; j < kMaxPR; ++j) {
+            const int s = (wvu + 4 * j) * spi + sub;
+            const int sc = s < nseg ? s : 0;
+            const int row = fdiv(sc, g.mCPL);
+            const int col = (sc - row * g.CPL) * g.SW + scol;
+            const int ci = fdiv(row, g.mIR);
+            const int ih = ih0 + row - ci * g.IR, iw = iw0 + col;
+            const bool placed = (s < nseg) & (col < g.IC);
+            const bool inimg = placed & (ih >= 0) & (ih < g.H) & (iw >= 0) & (iw < g.W);
+            xoff[j] = inimg ? esz * ((uint32_t)ci * plane + (uint32_t)(ih * g.W + iw)) : kMaskedOff;
+            const uint32_t li = (uint32_t)(placed ? ci * g.PSZ + (row - ci * g.IR) * g.IC + col : dummy);
+            if (j & 1) lidx[j >> 1] |= li << 16;
+            else lidx[j >> 1] = li;
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int co = ct + wvu + 4 * q + 16 * wcb;
+            woff[q] = co < g.Cout ? esz * ((uint32_t)co * wcs + (uint32_t)wkk) : kMaskedOff;
+        }
+    }
+    auto load_pf = [&](int c0) {
+        const uint32_t xsh = esz * (uint32_t)c0 * plane;
+        const uint32_t xlo = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)xn + xsh);
+        const uint32_t xhi = __builtin_amdgcn_readfirstlane((uint32_t)(((uintptr_t)xn + xsh) >> 32));
+        const uint32_t xnr = __builtin_amdgcn_readfirstlane(esz * (uint32_t)(g.Cin - c0) * plane);
+        const __amdgpu_buffer_rsrc_t xrc =
+            make_range_checked((const void *)(((uint64_t)xhi << 32) | xlo), xnr);
+#pragma unroll
+        for (int j = 0; j < kMaxPR; ++j) pr[j] = load_elem(xrc, xoff[j], x);
+        const uint32_t wsh = esz * (uint32_t)(c0 * T);
+        const uint32_t wlo = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)w + wsh);
+        const uint32_t whi = __builtin_amdgcn_readfirstlane((uint32_t)(((uintptr_t)w + wsh) >> 32));
+        const uint32_t wnr = __builtin_amdgcn_readfirstlane(
+            esz * (uint32_t)g.Cout * wcs - wsh);
+        const __amdgpu_buffer_rsrc_t wrc =
+            make_range_checked((const void *)(((uint64_t)whi << 32) | wlo), wnr);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int kb = 0; kb < kKB; ++kb)
+                wr[q * kKB + kb] = load_elem(wrc, woff[q] + esz * (uint32_t)(16 * kb), w);
+    };
+    auto store_pf = [&]() {
+#pragma unroll
+        for (int j = 0; j < kMaxPR; ++j)
+            smem[(j & 1) ? (lidx[j >> 1] >> 16) : (lidx[j >> 1] & 0xffffu)] = pr[j];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int kb = 0; kb < kKB; ++kb) {
+                const int k = 16 * kb + wkk;
+                const int wi = g.CK * g.PSZ + k * kWRS + (((wvu + 4 * q) << 2) | wcb);
+                smem[k < ckt ? wi : dummy] = wr[q * kKB + kb];
+            }
+    };
+
+    if constexpr (PF) load_pf(0);
     for (int c0 = 0; c0 < g.Cin; c0 += g.CK) {
         if (c0 > 0) __syncthreads();     // every wave is done with the previous chunk
         if constexpr (PF) {
-            store(0);
+            store_pf();
         } else {
             for (int p = 0; p < g.npass; ++p) {
                 load(c0, p);
@@ -247,7 +314,7 @@ __global__ __launch_bounds__(kThreads, 2) void conv_general(
         }
         __syncthreads();
         if constexpr (PF) {
-            if (c0 + g.CK < g.Cin) load(c0 + g.CK, 0);
+            if (c0 + g.CK < g.Cin) load_pf(c0 + g.CK);
         }
 
         // ---- MFMA over the chunk: step = (tap, 4-channel group cq), taps outer ----
@@ -391,7 +458,8 @@ bool plan(GenGeom &g, int epi, int &lds_bytes) {
                 const int64_t lim = mode < 2 ? 80 * 1024 : 160 * 1024;
                 for (int k = 16; k >= 4; k -= 4) {
                     if (k > cinp && k > 4) continue;
-                    const int64_t fill = ((int64_t)k * psz + (int64_t)T * k * kWRS) * 4;
+                    // patch + weights + a 64-word dummy area for the one-pass fill's stores
+                    const int64_t fill = ((int64_t)k * psz + (int64_t)T * k * kWRS + 64) * 4;
                     const int64_t need = epi == 0 && fill < kCoTile * kYS * 4 ? kCoTile * kYS * 4 : fill;
                     const int64_t npr = ((int64_t)k * ir * cpl + 4 * spi - 1) / (4 * spi);
                     const int64_t nkb = ((int64_t)k * T + 15) / 16;
