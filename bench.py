@@ -64,14 +64,14 @@ CONVT_BF16_BYTES = 128 * 64 * 64 * 64 * 2 + 128 * 128 * 129 * 129 * 2 + 64 * 128
 # x1.0.  `src` is the hash of the kernel's sources when the counters were taken; a
 # kernel edited since then reports traffic null.  See profiles/traffic_*.md.
 TRAFFIC = {
-"conv": {"src": "1ec6295bccaac937", "fetch_bytes": 266759109, "write_bytes": 130619504},
-    "conv_bf16": {"src": "1ec6295bccaac937", "fetch_bytes": 136677080, "write_bytes": 83626528},
-    "maxpool": {"src": "7af65d3a614e0202", "fetch_bytes": 2160262053, "write_bytes": 2140776592},
-    "maxpool_s2": {"src": "7af65d3a614e0202", "fetch_bytes": 2277432561, "write_bytes": 536870912},
-    "maxpool_d2": {"src": "7af65d3a614e0202", "fetch_bytes": 2670506204, "write_bytes": 2147483648},
-    "convT": {"src": "bc73f067020da62b", "fetch_bytes": 601323977, "write_bytes": 2356244736},
-    "convT_bf16": {"src": "c35853eab2c487e4", "fetch_bytes": 119830774, "write_bytes": 590036992},
-    "conv_general": {"src": "0e26e00736bf879f", "fetch_bytes": 137189000, "write_bytes": 69052544},
+    "conv": {"src": "b5b221991012a2b4", "fetch_bytes": 266713735, "write_bytes": 130700784},
+    "conv_bf16": {"src": "b5b221991012a2b4", "fetch_bytes": 136662745, "write_bytes": 82781424},
+    "maxpool": {"src": "7af65d3a614e0202", "fetch_bytes": 2160261989, "write_bytes": 2140678240},
+    "maxpool_s2": {"src": "7af65d3a614e0202", "fetch_bytes": 2277463088, "write_bytes": 536870912},
+    "maxpool_d2": {"src": "7af65d3a614e0202", "fetch_bytes": 2670600409, "write_bytes": 2147483648},
+    "convT": {"src": "bc73f067020da62b", "fetch_bytes": 603595392, "write_bytes": 2356611024},
+    "convT_bf16": {"src": "c35853eab2c487e4", "fetch_bytes": 119830774, "write_bytes": 590056224},
+    "conv_general": {"src": "bacb7064587111ac", "fetch_bytes": 136919505, "write_bytes": 69293488},
 }
 KERNEL_SOURCES = {
     "conv": ["conv_pool.hip", "ps_internal.h"],

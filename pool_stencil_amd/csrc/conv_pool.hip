@@ -41,6 +41,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace ps {
 namespace {
 
@@ -133,12 +135,22 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? PS_CONV_MIN_WAVES : 1)) void c
     const int ir0 = PK * ph - pad;
     const int ic0 = PK * pwt * G::T - pad;
     const float *xn = x + (size_t)n * Cin * H * W;
-    {
+    // (instantiated once per load width: a uniform test per element split the fill
+    // into one branch per load)
+    auto fill = [&](auto VEC) {
+        constexpr bool vec = decltype(VEC)::value;
         constexpr int NT = 64 * NPW;
         constexpr int NV = (G::COLS + 3) / 4;           // 4-column groups per tile row
         constexpr int TOTAL = CINP * G::ROWS * NV;
         constexpr int PER = (TOTAL + NT - 1) / NT;
-        const bool vec = ((ic0 & 3) == 0) && ((W & 3) == 0);
+        // Range-checked buffer loads over image n (below 2^31 bytes, host check): a value
+        // outside the image -- the conv's zero padding -- gets a masked offset and reads
+        // zero, so the loads are unconditional (bounds-checked loads compiled to a
+        // branch with about 50 instructions around each).  16-byte loads when the
+        // tile's columns are 16-byte aligned, else four 4-byte loads.
+        constexpr uint32_t kMasked = 0x80000000u;
+        const __amdgpu_buffer_rsrc_t xr =
+            make_range_checked(xn, 4u * (uint32_t)Cin * (uint32_t)H * (uint32_t)W);
         // loads are issued FB vectors at a time (all of them when FB >= PER)
         constexpr int FB = PS_CONV_FILL_BATCH > 0 && PS_CONV_FILL_BATCH < PER ? PS_CONV_FILL_BATCH : PER;
 #pragma unroll
@@ -152,18 +164,25 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? PS_CONV_MIN_WAVES : 1)) void c
                 const int r = row % G::ROWS;
                 const int ci = row / G::ROWS;
                 const int ir = ir0 + r, ic = ic0 + 4 * u;
-                const bool rok = i0 + ii < PER && e < TOTAL && ci < Cin && ir >= 0 && ir < H;
-                const float *src = xn + ((size_t)ci * H + ir) * W + ic;
-                float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (vec) {
-                    if (rok && ic >= 0 && ic < W) v = *(const float4 *)src;
-                } else if (rok) {
-                    if (ic >= 0 && ic < W) v.x = src[0];
-                    if (ic + 1 >= 0 && ic + 1 < W) v.y = src[1];
-                    if (ic + 2 >= 0 && ic + 2 < W) v.z = src[2];
-                    if (ic + 3 >= 0 && ic + 3 < W) v.w = src[3];
+                // (bitwise: a short-circuit chain compiles to branches)
+                const bool rok = (i0 + ii < PER) & (e < TOTAL) & (ci < Cin) & (ir >= 0) & (ir < H);
+                const uint32_t o = 4u * ((uint32_t)(ci * H + ir) * (uint32_t)W + (uint32_t)ic);
+                if constexpr (vec) {
+                    const bool ok = rok & (ic >= 0) & (ic < W);
+                    const uint4 q = __builtin_bit_cast(
+                        uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, ok ? o : kMasked, 0, 0));
+                    buf[ii] = make_float4(__uint_as_float(q.x), __uint_as_float(q.y),
+                                          __uint_as_float(q.z), __uint_as_float(q.w));
+                } else {
+                    float vv[4];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const bool ok = rok & (ic + k >= 0) & (ic + k < W);
+                        vv[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                            xr, ok ? o + 4u * k : kMasked, 0, 0));
+                    }
+                    buf[ii] = make_float4(vv[0], vv[1], vv[2], vv[3]);
                 }
-                buf[ii] = v;
             }
 #pragma unroll
             for (int ii = 0; ii < FB; ++ii) {
@@ -183,7 +202,11 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? PS_CONV_MIN_WAVES : 1)) void c
                 }
             }
         }
-    }
+    };
+    if (((ic0 & 3) == 0) && ((W & 3) == 0))
+        fill(std::true_type{});
+    else
+        fill(std::false_type{});
     __syncthreads();
 
     const int pw = pwt * G::T + 16 * wv + j;
@@ -291,7 +314,12 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? 2 : 1)) void conv_pool_bf16(
     // group of 8 columns is one 16-byte load per channel and lies wholly inside or
     // wholly outside the image; otherwise columns are loaded one by one.
 
-    // Load input row ir, columns [ic0 + 8u, ic0 + 8u + 8), all 8 channels.
+    // Load input row ir, columns [ic0 + 8u, ic0 + 8u + 8), all 8 channels.  VEC: one
+    // range-checked 16-byte buffer load per channel over image n (below 2^31 bytes,
+    // host check); a group outside the image or a channel >= Cin gets a masked offset
+    // and reads zero, so the loads are unconditional (no branch per load).
+    const __amdgpu_buffer_rsrc_t xr =
+        make_range_checked(xn, 2u * (uint32_t)Cin * (uint32_t)cstride);
     auto load_group = [&](int ir, int u, uint4 (&v)[8]) {
         const int ic = ic0 + 8 * u;
         const bool rok = ir >= 0 && ir < H;
@@ -300,7 +328,10 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? 2 : 1)) void conv_pool_bf16(
             v[ci] = make_uint4(0u, 0u, 0u, 0u);
             const uint16_t *src = xn + ci * cstride + (size_t)ir * W + ic;
             if constexpr (VEC) {
-                if (rok && ci < Cin && ic >= 0 && ic < W) v[ci] = *(const uint4 *)src;
+                const bool ok = rok & (ci < Cin) & (ic >= 0) & (ic < W);
+                const uint32_t o = 2u * ((uint32_t)ci * (uint32_t)cstride + (uint32_t)(ir * W + ic));
+                v[ci] = __builtin_bit_cast(
+                    uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, ok ? o : 0x80000000u, 0, 0));
             } else if (rok && ci < Cin) {
                 uint32_t hv[8];
 #pragma unroll
