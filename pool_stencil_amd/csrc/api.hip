@@ -126,8 +126,8 @@ int ps_conv_tanh_scale_bias_maxpool(const void *x, const void *w, const float *c
                           conv_pad <= 2 && Cin <= 8 && pool_stride == pool_k && pool_k >= 2 &&
                           pool_k <= 8 && pool_pad == 0 && pool_dil == 1 &&
                           (int64_t)Cin * H * W * (dtype == PS_F32 ? 4 : 2) < ((int64_t)1 << 31) &&
-                          (dtype == PS_F32 ||
-                           ((int64_t)Cout + 64) * PH * PW * 2 < ((int64_t)1 << 31));
+                          ((int64_t)Cout + 64) * PH * PW * (dtype == PS_F32 ? 4 : 2) <
+                              ((int64_t)1 << 31);
     if (small_k3)
         return ps::launch_conv_pool(x, w, conv_bias, bias2, y, dtype, N, Cin, H, W, Cout,
                                     conv_pad, OH, OW, scale, pool_k, PH, PW, (hipStream_t)stream);

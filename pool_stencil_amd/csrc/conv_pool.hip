@@ -85,7 +85,8 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? PS_CONV_MIN_WAVES : 1)) void c
     using G = TileGeom<PK, NPW>;
     constexpr int PS = pad_words_16mod64(G::ROWS * G::RS);  // words per input channel
     constexpr int CINP = 4 * CING;
-    __shared__ float tile[CINP * PS];
+    // the halo tile, and a 64-word dummy area for the fill's values with no place
+    __shared__ float tile[CINP * PS + 64];
     __shared__ float s_bias[2][64];  // conv bias, bias2 of the current 64-channel tile
 
     const uint32_t L = xcd_remap(blockIdx.x, gridDim.x);
@@ -184,20 +185,23 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? PS_CONV_MIN_WAVES : 1)) void c
                     buf[ii] = make_float4(vv[0], vv[1], vv[2], vv[3]);
                 }
             }
+            // LDS writes: a value past the tile's columns or past the last vector goes
+            // to the dummy area instead (no branches)
 #pragma unroll
             for (int ii = 0; ii < FB; ++ii) {
                 const int e = threadIdx.x + (i0 + ii) * NT;
-                if (i0 + ii < PER && e < TOTAL) {
+                if (i0 + ii < PER) {  // compile-time after unrolling
                     const int u = e % NV;
                     const int row = e / NV;
                     const int r = row % G::ROWS;
                     const int ci = row / G::ROWS;
-                    float *trow = tile + ci * PS + r * G::RS;
+                    const int tbase = ci * PS + r * G::RS;
                     const float vv[4] = {buf[ii].x, buf[ii].y, buf[ii].z, buf[ii].w};
 #pragma unroll
                     for (int k = 0; k < 4; ++k) {
                         const int c = 4 * u + k;
-                        if (c < G::COLS) trow[(c % PK) * G::Q + c / PK] = vv[k];
+                        const bool ok = (e < TOTAL) & (c < G::COLS);
+                        tile[ok ? tbase + (c % PK) * G::Q + c / PK : CINP * PS + (threadIdx.x & 63)] = vv[k];
                     }
                 }
             }
@@ -212,6 +216,11 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? PS_CONV_MIN_WAVES : 1)) void c
     const int pw = pwt * G::T + 16 * wv + j;
     const float *tb = tile + g4 * PS + 16 * wv + j;
     const float sgn = scale < 0.f ? -1.f : 1.f;
+    const uint32_t cplane = (uint32_t)(PH * PW);
+    const __amdgpu_buffer_rsrc_t yr =
+        make_range_checked(y + (size_t)n * Cout * cplane, 4u * (uint32_t)Cout * cplane);
+    const uint32_t lane_off =
+        pw < PW ? 4u * ((uint32_t)(4 * g4) * cplane + (uint32_t)(ph * PW + pw)) : 0x80000000u;
 
     for (int ct = 0; ct < Cout; ct += 64) {
         if (ct > 0) {
@@ -259,20 +268,20 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? PS_CONV_MIN_WAVES : 1)) void c
         }
 
         // ---- epilogue: conv bias, tanh, scale, bias2; D row 4*g4 + r = channel ----
-        if (pw < PW) {
+        // Range-checked buffer stores over image n's Cout planes: a column pw >= PW
+        // takes an offset past the end, and so does a channel >= Cout, so the stores
+        // are dropped without branches (the host keeps (Cout + 64) planes below 2^31
+        // bytes, so no offset wraps).
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt)
+        for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int cl = 16 * nt + 4 * g4 + r;
-                    const int co = ct + cl;
-                    if (co < Cout) {
-                        const float v = sgn * best[nt][r] + s_bias[0][cl];
-                        y[(((size_t)n * Cout + co) * PH + ph) * PW + pw] =
-                            tanh_exp(v) * scale + s_bias[1][cl];
-                    }
-                }
-        }
+            for (int r = 0; r < 4; ++r) {
+                const int cl = 16 * nt + 4 * g4 + r;
+                const float v = sgn * best[nt][r] + s_bias[0][cl];
+                __builtin_amdgcn_raw_buffer_store_b32(
+                    __float_as_uint(tanh_exp(v) * scale + s_bias[1][cl]), yr,
+                    lane_off + 4u * (uint32_t)(ct + 16 * nt + r) * cplane, 0, 0);
+            }
     }
 }
 
