@@ -88,6 +88,9 @@ constexpr int kWave = 64;
 #ifndef PS_MPSD_WGS_S2
 #define PS_MPSD_WGS_S2 2
 #endif
+#ifndef PS_MPSD_WGS_V1
+#define PS_MPSD_WGS_V1 0
+#endif
 // Waves (consecutive bands of one plane) per workgroup: all but the last hand their
 // halo rows over through LDS.  Measured on MI355X (k4 s1 p1, 32x64x512x512): one
 // 8-wave workgroup per CU beats 4 waves at 3 per CU by about 3%, and 16 resident
@@ -275,10 +278,22 @@ __global__ __launch_bounds__(kWave * PS_MAXPOOL_WG_WAVES) void maxpool_s1_rows(
 //     rows; whenever an input row completes output row oh (row oh*S - p + (K-1)*D),
 //     the vertical max over the ring's taps 0, D, .., (K-1)*D is written.
 // Neighbouring bands share (K-1)*D + 1 - S input rows, which both read.
-template <int K, int S, int D, int V, int PF>
+// EPI: the second stage of the page's unfused conv pipeline (l2_p82) on a stored
+// conv output: out = max over the window of tanh(x)*scale + bias2[c].  The window
+// reduces sgn*x (sgn = -1 when scale < 0: tanh and v -> v*scale + b are monotone,
+// so the max of the map is taken at the max of x for scale >= 0 and at the min for
+// scale < 0), and the map is applied once per output; an all-padding window stays
+// -inf.  C = channels (the plane's channel is plane % C).
+struct PoolEpi {
+    float sgn, scale;
+    const float *b2;
+    int C;
+};
+
+template <int K, int S, int D, int V, int PF, bool EPI>
 __global__ __launch_bounds__(256) void maxpool_rows_sd(
     const float *__restrict__ x, float *__restrict__ y, int H, int W, int OH, int OW, int pad,
-    int band_rows, int nbands, int nstrips, uint64_t ntasks) {
+    int band_rows, int nbands, int nstrips, uint64_t ntasks, PoolEpi epi) {
     constexpr int R = (K - 1) * D + 1;                        // input rows per window
     constexpr int SPAN = (kWave * V - 1) * S + (K - 1) * D + 1;  // input columns per strip
     constexpr int NCH = (SPAN + kWave - 1) / kWave;           // 64-column load chunks
@@ -309,12 +324,18 @@ __global__ __launch_bounds__(256) void maxpool_rows_sd(
         const int ic = ic0 + kWave * c + lane;
         colok[c] = ic >= 0 && ic < W;
     }
+    const float sgn = EPI ? epi.sgn : 1.f;
     auto load_row = [&](int ih, float (&v)[NCH]) {
         const bool rowok = ih >= 0 && ih < H;
         const float *rp = xp + (int64_t)ih * W + ic0 + lane;
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) v[c] = (rowok && colok[c]) ? rp[kWave * c] : -INFINITY;
+        for (int c = 0; c < NCH; ++c) {
+            v[c] = (rowok && colok[c]) ? rp[kWave * c] : -INFINITY;
+            if constexpr (EPI) v[c] = (rowok && colok[c]) ? sgn * v[c] : -INFINITY;
+        }
     };
+    float b2c = 0.f;
+    if constexpr (EPI) b2c = epi.b2[plane % (uint64_t)epi.C];
 
     float pf[PF][NCH];
 #pragma unroll
@@ -357,6 +378,8 @@ __global__ __launch_bounds__(256) void maxpool_rows_sd(
                     float m = ring[0][j];
 #pragma unroll
                     for (int kh = 1; kh < K; ++kh) m = fmax_ordered(m, ring[kh * D][j]);
+                    if constexpr (EPI)
+                        m = m == -INFINITY ? -INFINITY : tanh_exp(sgn * m) * epi.scale + b2c;
                     if (c0 + kWave * j + lane < OW) orow[kWave * j] = m;
                 }
             }
@@ -366,36 +389,47 @@ __global__ __launch_bounds__(256) void maxpool_rows_sd(
 
 int occupancy_cap_lds_bytes(int wgs);
 
-template <int K, int S, int D>
-int launch_rows_sd(const float *x, float *y, int N, int C, int H, int W, int OH, int OW, int p,
-                   hipStream_t stream) {
-    constexpr int V = PS_MPSD_V;
+template <int K, int S, int D, int V, bool EPI>
+int launch_rows_sd_v(const float *x, float *y, int N, int C, int H, int W, int OH, int OW, int p,
+                     const PoolEpi &epi, hipStream_t stream) {
     const int band_rows = S >= 2 ? PS_MPSD_BAND_S2 : PS_MPSD_BAND_S1;
     const int nbands = (OH + band_rows - 1) / band_rows;
     const int nstrips = (OW + kWave * V - 1) / (kWave * V);
     const uint64_t ntasks = (uint64_t)N * C * nstrips * nbands;
     const uint64_t nblocks = (ntasks + 3) / 4;
     if (nblocks > 0x7fffffffull) return PS_ERR_UNSUPPORTED;
-    const int lds_bytes = occupancy_cap_lds_bytes(S >= 2 ? PS_MPSD_WGS_S2 : PS_MPSD_WGS_S1);
+    // narrow strips keep little in flight per wave: no cap on resident workgroups
+    const int lds_bytes =
+        occupancy_cap_lds_bytes(V == 1 ? PS_MPSD_WGS_V1 : S >= 2 ? PS_MPSD_WGS_S2 : PS_MPSD_WGS_S1);
     if (lds_bytes > 65536 &&
-        hipFuncSetAttribute((const void *)maxpool_rows_sd<K, S, D, V, PS_MPSD_PF>,
+        hipFuncSetAttribute((const void *)maxpool_rows_sd<K, S, D, V, PS_MPSD_PF, EPI>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes) != hipSuccess)
         return PS_ERR_HIP;
-    hipLaunchKernelGGL((maxpool_rows_sd<K, S, D, V, PS_MPSD_PF>), dim3((unsigned)nblocks),
+    hipLaunchKernelGGL((maxpool_rows_sd<K, S, D, V, PS_MPSD_PF, EPI>), dim3((unsigned)nblocks),
                        dim3(256), lds_bytes, stream, x, y, H, W, OH, OW, p, band_rows, nbands,
-                       nstrips, ntasks);
+                       nstrips, ntasks, epi);
     return hipGetLastError() == hipSuccess ? PS_OK : PS_ERR_HIP;
 }
 
+// strips of 64 output columns for rows up to 64 wide (no idle chunks), else 256
+template <int K, int S, int D, bool EPI>
+int launch_rows_sd(const float *x, float *y, int N, int C, int H, int W, int OH, int OW, int p,
+                   const PoolEpi &epi, hipStream_t stream) {
+    if (OW <= 64) return launch_rows_sd_v<K, S, D, 1, EPI>(x, y, N, C, H, W, OH, OW, p, epi, stream);
+    return launch_rows_sd_v<K, S, D, PS_MPSD_V, EPI>(x, y, N, C, H, W, OH, OW, p, epi, stream);
+}
+
 // (K, S, D) combinations with a streaming kernel; -1 when there is none.
+template <bool EPI>
 int launch_rows_sd_any(const float *x, float *y, int N, int C, int H, int W, int OH, int OW,
-                       int k, int s, int p, int d, hipStream_t stream) {
-#define PS_SD(KK, SS, DD)                                                               \
-    if (k == KK && s == SS && d == DD)                                                  \
-        return launch_rows_sd<KK, SS, DD>(x, y, N, C, H, W, OH, OW, p, stream);
+                       int k, int s, int p, int d, const PoolEpi &epi, hipStream_t stream) {
+#define PS_SD(KK, SS, DD)                                                                      \
+    if (k == KK && s == SS && d == DD)                                                         \
+        return launch_rows_sd<KK, SS, DD, EPI>(x, y, N, C, H, W, OH, OW, p, epi, stream);
 #define PS_SD_K(SS, DD) PS_SD(2, SS, DD) PS_SD(3, SS, DD) PS_SD(4, SS, DD) PS_SD(5, SS, DD)
     PS_SD_K(2, 1)
     PS_SD_K(3, 1)
+    PS_SD_K(4, 1)
     PS_SD_K(1, 2)
     PS_SD_K(2, 2)
 #undef PS_SD_K
@@ -542,7 +576,8 @@ int launch_maxpool2d(const float *x, float *y, int N, int C, int H, int W, int O
         }
     }
     {
-        const int rc = launch_rows_sd_any(x, y, N, C, H, W, OH, OW, k, s, p, d, stream);
+        const int rc = launch_rows_sd_any<false>(x, y, N, C, H, W, OH, OW, k, s, p, d, PoolEpi{},
+                                                 stream);
         if (rc >= 0) return rc;
     }
     // output rows per thread: 8 at stride 1 (neighbouring rows share most input rows
@@ -577,6 +612,15 @@ int launch_maxpool2d(const float *x, float *y, int N, int C, int H, int W, int O
     }
 #undef PS_COLS
     return hipGetLastError() == hipSuccess ? PS_OK : PS_ERR_HIP;
+}
+
+// The fp32 tanh -> *scale -> +bias2 -> max-pool stage through the streaming kernel;
+// -1 when the window has no streaming instantiation.
+int launch_tanh_scale_bias_maxpool_rows(const float *y, const float *bias2, float *out, int N,
+                                        int C, int H, int W, int OH, int OW, float scale, int k,
+                                        int s, int p, int d, hipStream_t stream) {
+    const PoolEpi epi{scale < 0.f ? -1.f : 1.f, scale, bias2, C};
+    return launch_rows_sd_any<true>(y, out, N, C, H, W, OH, OW, k, s, p, d, epi, stream);
 }
 
 }  // namespace ps

@@ -45,6 +45,11 @@ int launch_convT(const float *x, const float *w, const float *convT_bias, float 
 int launch_tanh_scale_bias_maxpool(const void *y, const float *bias2, void *out, int dtype, int N,
                                    int C, int H, int W, int OH, int OW, float scale, int k, int s,
                                    int p, int d, hipStream_t stream);
+// The same stage for fp32 through the strided row-streaming max-pool kernel (k 2..5
+// with stride / dilation (2,1), (3,1), (4,1), (1,2), (2,2)); -1 for other windows.
+int launch_tanh_scale_bias_maxpool_rows(const float *y, const float *bias2, float *out, int N,
+                                        int C, int H, int W, int OH, int OW, float scale, int k,
+                                        int s, int p, int d, hipStream_t stream);
 int launch_softmax_bias_scale_sigmoid(const float *y, const float *bias2, float *out, int N,
                                       int C, int H, int W, float scale, hipStream_t stream);
 

@@ -8,8 +8,11 @@
 //   (floor mode, -inf padding; a window wholly in the padding gives -inf).
 //   As in the fused kernels, the window is reduced first (max of y for
 //   scale >= 0, min for scale < 0) and tanh is evaluated once per output: tanh
-//   and v -> v*scale + b are monotone.  One thread per output; the window is
-//   read through the cache hierarchy (the stored conv output is read once).
+//   and v -> v*scale + b are monotone.  fp32 windows with k 2..5 and stride /
+//   dilation (2,1), (3,1), (4,1), (1,2), (2,2) run on the row-streaming max-pool
+//   kernel with this map applied at its stores (each stored value read once).
+//   Other windows and bf16: one thread per output, the window read through the
+//   cache hierarchy.
 //
 // softmax_bias_scale_sigmoid (page Kimi-K2.6 l2_p91: the post-processing
 // kernel that runs in place on the stored transposed-conv output):
@@ -120,6 +123,12 @@ int launch_tanh_scale_bias_maxpool(const void *y, const float *bias2, void *out,
                                    int p, int d, hipStream_t stream) {
     const int64_t planes = (int64_t)N * C;
     if ((int64_t)OH * OW > 0x7fffffff - 256 || planes > 0x7fffffff) return PS_ERR_UNSUPPORTED;
+    if (dtype != PS_BF16) {  // fp32 windows the row-streaming kernel covers
+        const int rc = launch_tanh_scale_bias_maxpool_rows((const float *)y, bias2, (float *)out,
+                                                           N, C, H, W, OH, OW, scale, k, s, p, d,
+                                                           stream);
+        if (rc >= 0) return rc;
+    }
     const dim3 grid((unsigned)((OH * OW + 255) / 256), (unsigned)(planes < 65535 ? planes : 65535));
     if (dtype == PS_BF16)
         hipLaunchKernelGGL(tanh_scale_bias_maxpool_k<uint16_t>, grid, dim3(256), 0, stream,

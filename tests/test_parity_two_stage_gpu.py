@@ -81,6 +81,8 @@ POOL_EPI_CASES = [
     (1, 2, 20, 20, 3, 3, 1, 1, 0.0),
     (1, 3, 17, 300, 5, 1, 2, 1, 0.7),
     (1, 2, 6, 6, 2, 1, 2, 1, 2.0),      # windows wholly in the padding -> -inf
+    (1, 3, 150, 140, 4, 4, 1, 1, -0.6),  # row-streaming kernel: 5 bands, padding, scale < 0
+    (1, 2, 70, 600, 3, 2, 1, 1, 1.3),   # 256-column strips, a ragged second strip
 ]
 
 
