@@ -107,8 +107,9 @@ int ps_convT2d_out_dim(int in, int k, int stride, int pad, int output_padding, i
  * pool window / stride / padding / dilation are accepted, with two limits of
  * the tiling: the pool window's extent (pool_k-1)*pool_dil+1 must be <= 16, and
  * the conv input patch of one pooled output plus 64 x 4 x kH*kW weights must fit
- * the 160 KB of LDS of a compute unit (kH*kW <= 144 always does).  Beyond them
- * the call returns PS_ERR_UNSUPPORTED.  The 3x3, stride-1, dilation-1,
+ * the 160 KB of LDS of a compute unit (kH*kW <= 144 always does); and one image
+ * and the weight tensor must each be below 2^31 bytes (32-bit byte offsets).
+ * Beyond them the call returns PS_ERR_UNSUPPORTED.  The 3x3, stride-1, dilation-1,
  * conv_pad <= 2, Cin <= 8, disjoint-window (pool_stride = pool_k <= 8, no pool
  * padding or dilation) case runs a kernel of its own with the weights held in
  * registers; every other case runs the general tiled kernel. */
@@ -153,7 +154,10 @@ int ps_maxpool2d(const float *x, float *y, int N, int C, int H, int W, int k, in
  * x [N,Cin,H,W] float32, w [Cin,Cout,k,k] float32, convT_bias [Cout] float32 or NULL,
  * bias2 [Cout] float32, y [N,Cout,OH,OW] float32.
  * Supported: k = 4, stride = 2, pad = 1, dil = 1, output_padding in {0, 1},
- * Cout a multiple of 16 with 16 <= Cout <= 128, 1 <= Cin <= 256. */
+ * Cout a multiple of 16 with 16 <= Cout <= 128, 1 <= Cin <= 256 where one parity
+ * class's weights fit the LDS: (Cout*(16*Cq + 4) + 2*Cout)*4 <= 160 KB with
+ * Cq = max(ceil(Cin/4), 6) (Cin <= 76 at Cout = 128); x with its channels rounded
+ * up to 4*Cq, and y, below 2^29 elements each.  Beyond these PS_ERR_UNSUPPORTED. */
 int ps_convT_softmax_bias_scale_sigmoid(
     const float *x, const float *w, const float *convT_bias, const float *bias2, float *y,
     int N, int Cin, int H, int W, int Cout, int k, int stride, int pad, int output_padding,
