@@ -90,6 +90,8 @@ GENERAL_CASES = [
     dict(N=1, Cin=8, H=30, W=30, Cout=16, conv_bias=False, pool_k=3, pool_stride=3,
          pool_pad=1),
     dict(N=3, Cin=12, H=70, W=90, Cout=48, conv_pad=1, pool_k=2, pool_stride=1),  # many tiles
+    dict(N=2, Cin=20, H=26, W=30, Cout=72, conv_pad=1, pool_k=3, pool_stride=2,
+         pool_pad=1),                                                           # partial chunk, 2 images
 ]
 
 
