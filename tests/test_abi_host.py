@@ -106,6 +106,9 @@ def test_conv_pool_validation(ps):
     assert _conv(lib, pk=17, H=40, W=40) == ps.PS_ERR_UNSUPPORTED
     assert _conv(lib, pk=9, pd=2, H=40, W=40) == ps.PS_ERR_UNSUPPORTED
     assert _conv(lib, kH=13, kW=13, pk=2, H=64, W=64) == ps.PS_ERR_UNSUPPORTED
+    # one image of 2^31 bytes or more: the kernels' 32-bit byte offsets do not reach
+    assert _conv(lib, H=8192, W=8192) == ps.PS_ERR_UNSUPPORTED                # fp32, 8 ch
+    assert _conv(lib, dtype=1, Cin=16, H=8192, W=8192) == ps.PS_ERR_UNSUPPORTED  # bf16
     assert _conv(lib, x=MISALIGNED) == ps.PS_ERR_ALIGN
     assert _conv(lib, y=MISALIGNED) == ps.PS_ERR_ALIGN
     assert _conv(lib, kH=5, kW=5, y=MISALIGNED) == ps.PS_ERR_ALIGN
@@ -162,6 +165,8 @@ def test_convT_validation(ps):
     assert _convT(lib, s=3) == ps.PS_ERR_UNSUPPORTED
     assert _convT(lib, Cout=24) == ps.PS_ERR_UNSUPPORTED
     assert _convT(lib, Cout=144) == ps.PS_ERR_UNSUPPORTED
+    assert _convT(lib, Cin=80) == ps.PS_ERR_UNSUPPORTED     # a class's weights exceed the LDS
+    assert _convT(lib, Cin=76, Cout=128, N=1 << 12, H=64, W=64) == ps.PS_ERR_UNSUPPORTED  # >= 2^29
     assert _convT(lib, x=MISALIGNED) == ps.PS_ERR_ALIGN
 
 
