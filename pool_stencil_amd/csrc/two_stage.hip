@@ -61,9 +61,11 @@ __global__ __launch_bounds__(256) void tanh_scale_bias_maxpool_k(
     }
 }
 
+// sigmoid((e*inv + b) * scale) with the hardware reciprocal (the fused kernels use it
+// too; 1 ulp), not the IEEE division sequence.
 __device__ __forceinline__ float epilogue(float e, float inv, float b, float scale) {
     const float v = (e * inv + b) * scale;
-    return 1.f / (1.f + __expf(-v));
+    return __builtin_amdgcn_rcpf(1.f + __expf(-v));
 }
 
 // grid.x covers the HW pixels of an image, grid.y strides over the N images.
@@ -92,7 +94,7 @@ __global__ __launch_bounds__(256) void softmax_bias_scale_sigmoid_k(const float 
                 v[c] = c < C ? __expf(v[c] - mx) : 0.f;
                 sum += v[c];
             }
-            const float inv = 1.f / sum;
+            const float inv = __builtin_amdgcn_rcpf(sum);
 #pragma unroll
             for (int c = 0; c < CMAX; ++c)
                 if (c < C) out[base + (size_t)c * HW] = epilogue(v[c], inv, b2[c], scale);
@@ -107,7 +109,7 @@ __global__ __launch_bounds__(256) void softmax_bias_scale_sigmoid_k(const float 
                     sum += __expf(t - mx);
                 }
             }
-            const float inv = 1.f / sum;
+            const float inv = __builtin_amdgcn_rcpf(sum);
             for (int c = 0; c < C; ++c) {
                 const size_t i = base + (size_t)c * HW;
                 out[i] = epilogue(__expf(y[i] - mx), inv, b2[c], scale);
