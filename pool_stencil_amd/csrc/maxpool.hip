@@ -297,12 +297,20 @@ __global__ __launch_bounds__(256) void maxpool_rows_sd(
     constexpr int R = (K - 1) * D + 1;                        // input rows per window
     constexpr int SPAN = (kWave * V - 1) * S + (K - 1) * D + 1;  // input columns per strip
     constexpr int NCH = (SPAN + kWave - 1) / kWave;           // 64-column load chunks
+    constexpr int OV = R > S ? R - S : 0;                     // input rows shared with the band below
     __shared__ float lrow[4][NCH * kWave];                    // one row buffer per wave
+    // [wave][OV][V][64]: horizontal maxima of each band's first OV input rows, which
+    // are the last OV input rows of the band above it (the previous wave's)
+    __shared__ float lhalo[OV > 0 ? 4 * OV * V * kWave : 1];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x >> 6;
     const uint32_t blk = xcd_remap(blockIdx.x, gridDim.x);
     const uint64_t task = (uint64_t)blk * 4 + wave;
-    if (task >= ntasks) return;
+    // With a hand-over, every wave passes the kernel's one barrier exactly once.
+    if (task >= ntasks) {
+        if constexpr (OV > 0) __syncthreads();
+        return;
+    }
     const int band = (int)(task % (uint64_t)nbands);
     const uint64_t t2 = task / (uint64_t)nbands;
     const int strip = (int)(t2 % (uint64_t)nstrips);
@@ -316,6 +324,12 @@ __global__ __launch_bounds__(256) void maxpool_rows_sd(
     const int oh1 = min(OH, oh0 + band_rows);
     const int ih_first = oh0 * S - pad;
     const int nrows = (oh1 - 1 - oh0) * S + R;  // input rows of the band
+    // The next wave of the workgroup holds the band below in the same plane and strip:
+    // its first OV input rows are this band's last OV, whose horizontal maxima then come
+    // from the LDS instead of a second read.  Such a band has band_rows*S >= OV rows of
+    // its own to load (host check), so every wave reaches the barrier below.
+    const bool from_below = OV > 0 && wave + 1 < 4 && band + 1 < nbands;
+    const int nload = nrows - (from_below ? OV : 0);
     float *buf = lrow[wave];
 
     bool colok[NCH];
@@ -337,21 +351,46 @@ __global__ __launch_bounds__(256) void maxpool_rows_sd(
     float b2c = 0.f;
     if constexpr (EPI) b2c = epi.b2[plane % (uint64_t)epi.C];
 
+    // Append input row r's horizontal maxima to the ring of the last R and, when the
+    // row completes output row oh (row oh*S - p + (K-1)*D), write it.
+    float ring[R][V];
+    auto consume = [&](int r, const float (&hm)[V]) {
+#pragma unroll
+        for (int i = 0; i < R - 1; ++i)
+#pragma unroll
+            for (int j = 0; j < V; ++j) ring[i][j] = ring[i + 1][j];
+#pragma unroll
+        for (int j = 0; j < V; ++j) ring[R - 1][j] = hm[j];
+        const int q = r - (R - 1);  // = (oh - oh0) * S when row r completes output oh
+        if (q >= 0 && q % S == 0) {
+            const int oh = oh0 + q / S;
+            float *orow = yp + (int64_t)oh * OW + c0 + lane;
+#pragma unroll
+            for (int j = 0; j < V; ++j) {
+                float m = ring[0][j];
+#pragma unroll
+                for (int kh = 1; kh < K; ++kh) m = fmax_ordered(m, ring[kh * D][j]);
+                if constexpr (EPI)
+                    m = m == -INFINITY ? -INFINITY : tanh_exp(sgn * m) * epi.scale + b2c;
+                if (c0 + kWave * j + lane < OW) orow[kWave * j] = m;
+            }
+        }
+    };
+
     float pf[PF][NCH];
 #pragma unroll
     for (int s = 0; s < PF; ++s)
-        if (s < nrows) load_row(ih_first + s, pf[s]);
+        if (s < nload) load_row(ih_first + s, pf[s]);
 
-    float ring[R][V];
-    for (int base = 0; base < nrows; base += PF) {
+    for (int base = 0; base < nload; base += PF) {
 #pragma unroll
         for (int s = 0; s < PF; ++s) {
             const int r = base + s;
-            if (r >= nrows) break;
+            if (r >= nload) break;
             // the row into the wave's LDS buffer, the slot refilled PF rows further down
 #pragma unroll
             for (int c = 0; c < NCH; ++c) buf[kWave * c + lane] = pf[s][c];
-            if (r + PF < nrows) load_row(ih_first + r + PF, pf[s]);
+            if (r + PF < nload) load_row(ih_first + r + PF, pf[s]);
             __builtin_amdgcn_wave_barrier();
             float hm[V];
 #pragma unroll
@@ -363,44 +402,52 @@ __global__ __launch_bounds__(256) void maxpool_rows_sd(
                 hm[j] = m;
             }
             __builtin_amdgcn_wave_barrier();  // the next row's writes come after these reads
+            if constexpr (OV > 0) {
+                // hand the first OV rows to the band above (the previous wave)
+                if (r < OV && wave > 0) {
 #pragma unroll
-            for (int i = 0; i < R - 1; ++i)
-#pragma unroll
-                for (int j = 0; j < V; ++j) ring[i][j] = ring[i + 1][j];
-#pragma unroll
-            for (int j = 0; j < V; ++j) ring[R - 1][j] = hm[j];
-            const int q = r - (R - 1);  // = (oh - oh0) * S when row r completes output oh
-            if (q >= 0 && q % S == 0) {
-                const int oh = oh0 + q / S;
-                float *orow = yp + (int64_t)oh * OW + c0 + lane;
-#pragma unroll
-                for (int j = 0; j < V; ++j) {
-                    float m = ring[0][j];
-#pragma unroll
-                    for (int kh = 1; kh < K; ++kh) m = fmax_ordered(m, ring[kh * D][j]);
-                    if constexpr (EPI)
-                        m = m == -INFINITY ? -INFINITY : tanh_exp(sgn * m) * epi.scale + b2c;
-                    if (c0 + kWave * j + lane < OW) orow[kWave * j] = m;
+                    for (int j = 0; j < V; ++j)
+                        lhalo[((wave * OV + r) * V + j) * kWave + lane] = hm[j];
                 }
+                if (r == OV - 1) __syncthreads();
+            }
+            consume(r, hm);
+        }
+    }
+    if constexpr (OV > 0) {
+        if (from_below) {
+            for (int i = 0; i < OV; ++i) {
+                float hm[V];
+#pragma unroll
+                for (int j = 0; j < V; ++j)
+                    hm[j] = lhalo[(((wave + 1) * OV + i) * V + j) * kWave + lane];
+                consume(nload + i, hm);
             }
         }
     }
 }
 
-int occupancy_cap_lds_bytes(int wgs);
+int occupancy_cap_lds_bytes(int wgs, int static_bytes);
 
 template <int K, int S, int D, int V, bool EPI>
 int launch_rows_sd_v(const float *x, float *y, int N, int C, int H, int W, int OH, int OW, int p,
                      const PoolEpi &epi, hipStream_t stream) {
     const int band_rows = S >= 2 ? PS_MPSD_BAND_S2 : PS_MPSD_BAND_S1;
+    // the kernel's static LDS (row buffers and the halo hand-over), as declared there
+    constexpr int R = (K - 1) * D + 1;
+    constexpr int NCH = ((kWave * V - 1) * S + (K - 1) * D + 1 + kWave - 1) / kWave;
+    constexpr int OV = R > S ? R - S : 0;
+    constexpr int static_bytes = 4 * (4 * NCH * kWave + (OV > 0 ? 4 * OV * V * kWave : 1));
+    // a band that hands rows over must load at least OV rows of its own
+    if (band_rows * S < OV) return PS_ERR_UNSUPPORTED;
     const int nbands = (OH + band_rows - 1) / band_rows;
     const int nstrips = (OW + kWave * V - 1) / (kWave * V);
     const uint64_t ntasks = (uint64_t)N * C * nstrips * nbands;
     const uint64_t nblocks = (ntasks + 3) / 4;
     if (nblocks > 0x7fffffffull) return PS_ERR_UNSUPPORTED;
     // narrow strips keep little in flight per wave: no cap on resident workgroups
-    const int lds_bytes =
-        occupancy_cap_lds_bytes(V == 1 ? PS_MPSD_WGS_V1 : S >= 2 ? PS_MPSD_WGS_S2 : PS_MPSD_WGS_S1);
+    const int lds_bytes = occupancy_cap_lds_bytes(
+        V == 1 ? PS_MPSD_WGS_V1 : S >= 2 ? PS_MPSD_WGS_S2 : PS_MPSD_WGS_S1, static_bytes);
     if (lds_bytes > 65536 &&
         hipFuncSetAttribute((const void *)maxpool_rows_sd<K, S, D, V, PS_MPSD_PF, EPI>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes) != hipSuccess)
@@ -514,15 +561,16 @@ __global__ __launch_bounds__(256) void maxpool_cols(const float *__restrict__ x,
     }
 }
 
-// Dynamic LDS bytes that leave room for exactly `wgs` workgroups per CU (0: no cap).
-int occupancy_cap_lds_bytes(int wgs) {
+// Dynamic LDS bytes that, with the kernel's static LDS, leave room for exactly `wgs`
+// workgroups per CU (0: no cap).
+int occupancy_cap_lds_bytes(int wgs, int static_bytes) {
     if (wgs <= 0) return 0;
     int dev = 0, lds = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
         hipSuccess)
         return 0;
-    const int share = lds / wgs - 12 * 1024;  // below the share, static LDS included
+    const int share = lds / wgs - static_bytes - 512;  // 512 B of allocation slack
     return share > 0 ? share : 0;
 }
 
@@ -538,7 +586,7 @@ int launch_rows(const float *x, float *y, int N, int C, int H, int W, int OH, in
     if (nblocks > 0x7fffffffull) return PS_ERR_UNSUPPORTED;
     // the halo hand-over buffer, at least the occupancy cap's LDS share
     const int halo_bytes = nw * (K - 1) * V * kWave * (int)sizeof(float);
-    const int cap_bytes = occupancy_cap_lds_bytes(PS_MAXPOOL_WGS_PER_CU);
+    const int cap_bytes = occupancy_cap_lds_bytes(PS_MAXPOOL_WGS_PER_CU, 0);
     const int lds_bytes = cap_bytes > halo_bytes ? cap_bytes : halo_bytes;
     if (lds_bytes > 65536 &&
         hipFuncSetAttribute((const void *)maxpool_s1_rows<K, V, PS_MAXPOOL_PREFETCH>,
