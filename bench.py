@@ -64,14 +64,14 @@ CONVT_BF16_BYTES = 128 * 64 * 64 * 64 * 2 + 128 * 128 * 129 * 129 * 2 + 64 * 128
 # x1.0.  `src` is the hash of the kernel's sources when the counters were taken; a
 # kernel edited since then reports traffic null.  See profiles/traffic_*.md.
 TRAFFIC = {
-    "conv": {"src": "1f50f3979f93e5bd", "fetch_bytes": 266684040, "write_bytes": 130621648},
-    "conv_bf16": {"src": "1f50f3979f93e5bd", "fetch_bytes": 136659673, "write_bytes": 82682736},
-    "maxpool": {"src": "ae3c7bf4d49a6384", "fetch_bytes": 2160265253, "write_bytes": 2140680160},
-    "maxpool_s2": {"src": "ae3c7bf4d49a6384", "fetch_bytes": 2176875727, "write_bytes": 536870912},
-    "maxpool_d2": {"src": "ae3c7bf4d49a6384", "fetch_bytes": 2266875460, "write_bytes": 2147483648},
-    "convT": {"src": "f6e144b9d0e20781", "fetch_bytes": 596847385, "write_bytes": 2354175728},
-    "convT_bf16": {"src": "4dd80d9c4526d1a3", "fetch_bytes": 119830774, "write_bytes": 589927120},
-    "conv_general": {"src": "683da3031f3318fe", "fetch_bytes": 136918737, "write_bytes": 69294320},
+    "conv": {"src": "0acc808eaefeb300", "fetch_bytes": 266696327, "write_bytes": 130619552},
+    "conv_bf16": {"src": "0acc808eaefeb300", "fetch_bytes": 136697560, "write_bytes": 81664352},
+    "maxpool": {"src": "ae3c7bf4d49a6384", "fetch_bytes": 2160265061, "write_bytes": 2140786784},
+    "maxpool_s2": {"src": "ae3c7bf4d49a6384", "fetch_bytes": 2176868175, "write_bytes": 536870912},
+    "maxpool_d2": {"src": "ae3c7bf4d49a6384", "fetch_bytes": 2266535119, "write_bytes": 2147483648},
+    "convT": {"src": "f6e144b9d0e20781", "fetch_bytes": 590584866, "write_bytes": 2346399040},
+    "convT_bf16": {"src": "4dd80d9c4526d1a3", "fetch_bytes": 119830774, "write_bytes": 590347648},
+    "conv_general": {"src": "683da3031f3318fe", "fetch_bytes": 136918993, "write_bytes": 69310592},
 }
 KERNEL_SOURCES = {
     "conv": ["conv_pool.hip", "ps_internal.h"],

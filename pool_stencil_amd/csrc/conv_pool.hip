@@ -73,6 +73,9 @@ struct TileGeom {
 #ifndef PS_CONV_DXG
 #define PS_CONV_DXG 0
 #endif
+#ifndef PS_BF16_LDS_AHEAD
+#define PS_BF16_LDS_AHEAD 3
+#endif
 #ifndef PS_CONV_MIN_WAVES
 #define PS_CONV_MIN_WAVES 3
 #endif
@@ -484,32 +487,72 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? 2 : 1)) void conv_pool_bf16(
                 stage_bias(ct);
                 __syncthreads();
             }
+            // The pooled row's B fragments stream from the ring in (dy, dx, s) order, each
+            // read AHEAD fragments before its four MFMAs, so the matrix cores do not wait
+            // on LDS latency.  Position p = dy*PK + dx accumulates into acc[p % 3]; the
+            // pool max of positions p-2 and p-1 (one v_max3 per value) is taken after
+            // position p's first MFMAs, when their results are long complete.
+            constexpr int NPOS = PK * PK;
+            constexpr int NFR = 3 * NPOS;
+            constexpr int AHEAD_REQ = (MULTI || !VEC) && PS_BF16_LDS_AHEAD > 2 ? 2 : PS_BF16_LDS_AHEAD;
+            constexpr int AHEAD = AHEAD_REQ < NFR ? AHEAD_REQ : NFR;
+            int ridx[3][PK];  // ring entry index of kernel row khs[s] for window row dy
+            {
+                const int rb = ((rbase % RING) + RING) % RING;
+#pragma unroll
+                for (int s = 0; s < 3; ++s)
+#pragma unroll
+                    for (int dy = 0; dy < PK; ++dy) {
+                        const int r = rb + dy + khs[s];
+                        ridx[s][dy] = (r >= RING ? r - RING : r) * G::RS;
+                    }
+            }
+            auto frag = [&](int f) {
+                const int pp = f / 3, s = f % 3;
+                return __builtin_bit_cast(bf16x8, ring[ridx[s][pp / PK] + coff[s][pp % PK]]);
+            };
             f32x4 best[4];
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) best[nt] = (f32x4){-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-#pragma unroll 1
-            for (int dy = 0; dy < PK; ++dy) {
-                const uint4 *rows[3];
+            f32x4 acc[3][4];
+            bf16x8 bq[AHEAD];
 #pragma unroll
-                for (int s = 0; s < 3; ++s) rows[s] = ring + ((rbase + dy + khs[s] + 4 * RING) % RING) * G::RS;
+            for (int f = 0; f < AHEAD; ++f) bq[f] = frag(f);
 #pragma unroll
-                for (int dx = 0; dx < PK; ++dx) {
-                    f32x4 acc[4];
+            for (int f = 0; f < NFR; ++f) {
+                const int pp = f / 3, s = f % 3;
+                const bf16x8 b = bq[f % AHEAD];
+                if (f + AHEAD < NFR) bq[f % AHEAD] = frag(f + AHEAD);
 #pragma unroll
-                    for (int nt = 0; nt < 4; ++nt) acc[nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int s = 0; s < 3; ++s) {
-                        const bf16x8 b = __builtin_bit_cast(bf16x8, rows[s][coff[s][dx]]);
-#pragma unroll
-                        for (int nt = 0; nt < 4; ++nt)
-                            acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[nt][s], b, acc[nt], 0, 0, 0);
-                    }
+                for (int nt = 0; nt < 4; ++nt)
+                    acc[pp % 3][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        wa[nt][s], b, s == 0 ? (f32x4){0.f, 0.f, 0.f, 0.f} : acc[pp % 3][nt], 0, 0, 0);
+                if (s == 0 && pp >= 2 && pp % 2 == 0) {
 #pragma unroll
                     for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) best[nt][r] = fmaxf(best[nt][r], acc[nt][r]);
+                        for (int r = 0; r < 4; ++r)
+                            best[nt][r] = fmaxf(fmaxf(best[nt][r], acc[(pp - 2) % 3][nt][r]),
+                                                acc[(pp - 1) % 3][nt][r]);
+                    // an empty volatile asm that takes the maxima as operands keeps them
+                    // in this step (pure arithmetic would otherwise sink to the epilogue
+                    // and hold every position's sums live)
+#pragma unroll
+                    for (int nt = 0; nt < 4; ++nt)
+                        asm volatile("" : "+v"(best[nt]));
                 }
+                __builtin_amdgcn_sched_barrier(0);
             }
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    if constexpr (NPOS % 2 == 0)
+                        best[nt][r] = fmaxf(fmaxf(best[nt][r], acc[(NPOS - 2) % 3][nt][r]),
+                                            acc[(NPOS - 1) % 3][nt][r]);
+                    else
+                        best[nt][r] = fmaxf(best[nt][r], acc[(NPOS - 1) % 3][nt][r]);
+                }
             // One channel tile: write the prefetched rows to the ring before the output
             // stores (their ring slots are not read by row ph), so that waiting for the
             // loads does not also wait for the output stores (on this chip a wait on a
