@@ -73,6 +73,9 @@ struct TileGeom {
 #ifndef PS_CONV_DXG
 #define PS_CONV_DXG 0
 #endif
+#ifndef PS_BF16_MAX_STEP
+#define PS_BF16_MAX_STEP 1
+#endif
 #ifndef PS_BF16_LDS_AHEAD
 #define PS_BF16_LDS_AHEAD 3
 #endif
@@ -527,7 +530,7 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? 2 : 1)) void conv_pool_bf16(
                 for (int nt = 0; nt < 4; ++nt)
                     acc[pp % 3][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                         wa[nt][s], b, s == 0 ? (f32x4){0.f, 0.f, 0.f, 0.f} : acc[pp % 3][nt], 0, 0, 0);
-                if (s == 0 && pp >= 2 && pp % 2 == 0) {
+                if (s == PS_BF16_MAX_STEP && pp >= 2 && pp % 2 == 0) {
 #pragma unroll
                     for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
