@@ -169,6 +169,8 @@ CONV_CASES = [
     dict(N=1, Cin=8, H=19, W=33, Cout=32, conv_pad=2),
     dict(N=1, Cin=8, H=40, W=90, Cout=16, pool_k=2, pool_stride=2),
     dict(N=1, Cin=4, H=40, W=90, Cout=16, pool_k=3, pool_stride=3),
+    dict(N=2, Cin=8, H=52, W=200, Cout=64, pool_k=3, pool_stride=3),  # 16-byte rows, k3
+    dict(N=1, Cin=8, H=37, W=136, Cout=96, pool_k=3, pool_stride=3),  # 16-byte rows, 2 tiles
     dict(N=1, Cin=8, H=50, W=77, Cout=24, pool_k=5, pool_stride=5),
     dict(N=1, Cin=8, H=50, W=140, Cout=16, pool_k=6, pool_stride=6),
     dict(N=1, Cin=7, H=40, W=60, Cout=16, pool_k=7, pool_stride=7),
