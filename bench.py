@@ -64,14 +64,14 @@ CONVT_BF16_BYTES = 128 * 64 * 64 * 64 * 2 + 128 * 128 * 129 * 129 * 2 + 64 * 128
 # x1.0.  `src` is the hash of the kernel's sources when the counters were taken; a
 # kernel edited since then reports traffic null.  See profiles/traffic_*.md.
 TRAFFIC = {
-    "conv": {"src": "4abb9dbd2135585a", "fetch_bytes": 266696327, "write_bytes": 130615504},
-    "conv_bf16": {"src": "4abb9dbd2135585a", "fetch_bytes": 136703704, "write_bytes": 81272912},
-    "maxpool": {"src": "ae3c7bf4d49a6384", "fetch_bytes": 2160265061, "write_bytes": 2140662832},
-    "maxpool_s2": {"src": "ae3c7bf4d49a6384", "fetch_bytes": 2176850768, "write_bytes": 536870912},
-    "maxpool_d2": {"src": "ae3c7bf4d49a6384", "fetch_bytes": 2266786375, "write_bytes": 2147483648},
-    "convT": {"src": "f6e144b9d0e20781", "fetch_bytes": 592997140, "write_bytes": 2344990784},
-    "convT_bf16": {"src": "4dd80d9c4526d1a3", "fetch_bytes": 119830774, "write_bytes": 590002368},
-    "conv_general": {"src": "683da3031f3318fe", "fetch_bytes": 136923089, "write_bytes": 69311152},
+    "conv": {"src": "f76c9968fdaf4a7a", "fetch_bytes": 266696327, "write_bytes": 130622128},
+    "conv_bf16": {"src": "f76c9968fdaf4a7a", "fetch_bytes": 136702680, "write_bytes": 79888640},
+    "maxpool": {"src": "ae3c7bf4d49a6384", "fetch_bytes": 2160264933, "write_bytes": 2140748608},
+    "maxpool_s2": {"src": "ae3c7bf4d49a6384", "fetch_bytes": 2176842384, "write_bytes": 536870912},
+    "maxpool_d2": {"src": "ae3c7bf4d49a6384", "fetch_bytes": 2266536591, "write_bytes": 2147483648},
+    "convT": {"src": "f6e144b9d0e20781", "fetch_bytes": 606928661, "write_bytes": 2347996928},
+    "convT_bf16": {"src": "4dd80d9c4526d1a3", "fetch_bytes": 119830774, "write_bytes": 589754400},
+    "conv_general": {"src": "683da3031f3318fe", "fetch_bytes": 136918929, "write_bytes": 69299472},
 }
 KERNEL_SOURCES = {
     "conv": ["conv_pool.hip", "ps_internal.h"],

@@ -309,6 +309,15 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? 2 : 1)) void conv_pool_bf16(
     constexpr int NG = (G::COLS + 7) / 8;   // 8-column groups per tile row
     __shared__ uint4 ring[RING * G::RS];
     __shared__ float s_bias[2][64];
+    constexpr int NTOT = PK * NG;           // 8-column groups of the PK rows a pooled row adds
+    constexpr int NPER = (NTOT + NT - 1) / NT;
+    // VEC: the rows of the next pooled row are loaded straight into LDS (buffer loads
+    // with the LDS flag, range-checked like the register loads).  A lane's 16 bytes
+    // land in its own slot, stage[i][wave][ci][lane], so each thread reads back only
+    // what it loaded itself, after its own loads have completed: no barrier, and no
+    // registers held across the MFMA stream.
+    __shared__ uint4 stage[VEC ? NPER : 1][NPW][8][64];
+    const int wvu = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
     // ---- work item: (image n, column strip pwt, pooled rows [p0, p1)) ----
     const uint32_t L = xcd_remap(blockIdx.x, gridDim.x);
@@ -469,16 +478,29 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? 2 : 1)) void conv_pool_bf16(
 
     for (int ph = p0; ph < p1; ++ph) {
         // issue the loads of the PK rows that pooled row ph + 1 adds
-        constexpr int NTOT = PK * NG;
-        constexpr int NPER = (NTOT + NT - 1) / NT;
-        uint4 pre[NPER][8];
+        uint4 pre[VEC ? 1 : NPER][8];  // unaligned rows: loaded into registers
         const int nr0 = PK * (ph + 1) - pad + 2;
         const bool more = ph + 1 < p1;
         if (more) {
 #pragma unroll
             for (int i = 0; i < NPER; ++i) {
                 const int e = threadIdx.x + i * NT;
-                if (e < NTOT) load_group(nr0 + e / NG, e % NG, pre[i]);
+                if (e < NTOT) {
+                    if constexpr (VEC) {
+                        const int ir = nr0 + e / NG, ic = ic0 + 8 * (e % NG);
+                        const bool rok = ir >= 0 && ir < H;
+#pragma unroll
+                        for (int ci = 0; ci < 8; ++ci) {
+                            const bool ok = rok & (ci < Cin) & (ic >= 0) & (ic < W);
+                            const uint32_t o = 2u * ((uint32_t)ci * (uint32_t)cstride + (uint32_t)(ir * W + ic));
+                            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                                xr, (__attribute__((address_space(3))) void *)&stage[i][wvu][ci][0], 16,
+                                ok ? o : 0x80000000u, 0, 0, 0);
+                        }
+                    } else {
+                        load_group(nr0 + e / NG, e % NG, pre[i]);
+                    }
+                }
             }
         }
 
@@ -564,7 +586,17 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? 2 : 1)) void conv_pool_bf16(
 #pragma unroll
                 for (int i = 0; i < NPER; ++i) {
                     const int e = threadIdx.x + i * NT;
-                    if (e < NTOT) store_group(nr0 + e / NG, e % NG, pre[i]);
+                    if (e < NTOT) {
+                        if constexpr (VEC) {
+                            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's loads have landed
+                            uint4 v[8];
+#pragma unroll
+                            for (int ci = 0; ci < 8; ++ci) v[ci] = stage[i][wvu][ci][lane];
+                            store_group(nr0 + e / NG, e % NG, v);
+                        } else {
+                            store_group(nr0 + e / NG, e % NG, pre[i]);
+                        }
+                    }
                 }
             }
             // output (n, co = ct + 16 nt + 4 g4 + r, ph, pw)
@@ -589,7 +621,17 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? 2 : 1)) void conv_pool_bf16(
 #pragma unroll
             for (int i = 0; i < NPER; ++i) {
                 const int e = threadIdx.x + i * NT;
-                if (e < NTOT) store_group(nr0 + e / NG, e % NG, pre[i]);
+                if (e < NTOT) {
+                    if constexpr (VEC) {
+                        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's loads have landed
+                        uint4 v[8];
+#pragma unroll
+                        for (int ci = 0; ci < 8; ++ci) v[ci] = stage[i][wvu][ci][lane];
+                        store_group(nr0 + e / NG, e % NG, v);
+                    } else {
+                        store_group(nr0 + e / NG, e % NG, pre[i]);
+                    }
+                }
             }
         }
         __syncthreads();
