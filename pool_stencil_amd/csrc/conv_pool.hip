@@ -316,7 +316,7 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? 2 : 1)) void conv_pool_bf16(
     // land in its own slot, stage[i][wave][ci][lane], so each thread reads back only
     // what it loaded itself, after its own loads have completed: no barrier, and no
     // registers held across the MFMA stream.
-    __shared__ uint4 stage[VEC ? NPER : 1][NPW][8][64];
+    __shared__ uint4 stage[VEC ? NPER : 1][VEC ? NPW : 1][8][VEC ? 64 : 1];
     const int wvu = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
     // ---- work item: (image n, column strip pwt, pooled rows [p0, p1)) ----
@@ -521,6 +521,9 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? 2 : 1)) void conv_pool_bf16(
             constexpr int NFR = 3 * NPOS;
             constexpr int AHEAD_REQ = (MULTI || !VEC) && PS_BF16_LDS_AHEAD > 2 ? 2 : PS_BF16_LDS_AHEAD;
             constexpr int AHEAD = AHEAD_REQ < NFR ? AHEAD_REQ : NFR;
+            // the variants with more live registers (row loads held in registers, or
+            // several channel tiles) take the pool max at the first K-step
+            constexpr int MAX_STEP = (MULTI || !VEC) ? 0 : PS_BF16_MAX_STEP;
             int ridx[3][PK];  // ring entry index of kernel row khs[s] for window row dy
             {
                 const int rb = ((rbase % RING) + RING) % RING;
@@ -552,7 +555,7 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? 2 : 1)) void conv_pool_bf16(
                 for (int nt = 0; nt < 4; ++nt)
                     acc[pp % 3][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                         wa[nt][s], b, s == 0 ? (f32x4){0.f, 0.f, 0.f, 0.f} : acc[pp % 3][nt], 0, 0, 0);
-                if (s == PS_BF16_MAX_STEP && pp >= 2 && pp % 2 == 0) {
+                if (s == MAX_STEP && pp >= 2 && pp % 2 == 0) {
 #pragma unroll
                     for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
