@@ -64,14 +64,14 @@ CONVT_BF16_BYTES = 128 * 64 * 64 * 64 * 2 + 128 * 128 * 129 * 129 * 2 + 64 * 128
 # x1.0.  `src` is the hash of the kernel's sources when the counters were taken; a
 # kernel edited since then reports traffic null.  See profiles/traffic_*.md.
 TRAFFIC = {
-    "conv": {"src": "fdb9b61b82b76488", "fetch_bytes": 266687112, "write_bytes": 130620736},
-    "conv_bf16": {"src": "fdb9b61b82b76488", "fetch_bytes": 136709847, "write_bytes": 79990448},
-    "maxpool": {"src": "ae3c7bf4d49a6384", "fetch_bytes": 2160264741, "write_bytes": 2140794064},
-    "maxpool_s2": {"src": "ae3c7bf4d49a6384", "fetch_bytes": 2176855376, "write_bytes": 536870912},
-    "maxpool_d2": {"src": "ae3c7bf4d49a6384", "fetch_bytes": 2266701897, "write_bytes": 2147483648},
-    "convT": {"src": "f6e144b9d0e20781", "fetch_bytes": 590432103, "write_bytes": 2348765648},
-    "convT_bf16": {"src": "4dd80d9c4526d1a3", "fetch_bytes": 119830774, "write_bytes": 590149984},
-    "conv_general": {"src": "683da3031f3318fe", "fetch_bytes": 136919377, "write_bytes": 69312240},
+    "conv": {"src": "56935f836ef1ce8d", "fetch_bytes": 266687112, "write_bytes": 130625824},
+    "conv_bf16": {"src": "56935f836ef1ce8d", "fetch_bytes": 136709847, "write_bytes": 79985968},
+    "maxpool": {"src": "ae3c7bf4d49a6384", "fetch_bytes": 2160264933, "write_bytes": 2140766640},
+    "maxpool_s2": {"src": "ae3c7bf4d49a6384", "fetch_bytes": 2176859472, "write_bytes": 536870912},
+    "maxpool_d2": {"src": "ae3c7bf4d49a6384", "fetch_bytes": 2266622156, "write_bytes": 2147483648},
+    "convT": {"src": "f6e144b9d0e20781", "fetch_bytes": 596515363, "write_bytes": 2346226880},
+    "convT_bf16": {"src": "4dd80d9c4526d1a3", "fetch_bytes": 119830774, "write_bytes": 589941136},
+    "conv_general": {"src": "683da3031f3318fe", "fetch_bytes": 136919185, "write_bytes": 69272144},
 }
 KERNEL_SOURCES = {
     "conv": ["conv_pool.hip", "ps_internal.h"],

@@ -296,8 +296,9 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? PS_CONV_MIN_WAVES : 1)) void c
 // rows [p0, p1) of one image and one 16*NPW-column strip.  Its weights are loaded
 // once.  Input rows live in an LDS ring of 2*PK + 2 rows (channel-last entries of
 // 8 bf16): pooled row ph reads ring rows PK*ph - pad ... + PK + 1, while the PK
-// rows that pooled row ph+1 adds are loaded from HBM into registers during the
-// MFMA work of row ph and written to the ring afterwards.  One barrier per row.
+// rows that pooled row ph+1 adds are loaded from HBM during the MFMA work of row ph
+// (into an LDS staging area when rows are 16-byte aligned, else into registers) and
+// transposed into the ring afterwards.  One barrier per row.
 template <int PK, int NPW, bool VEC, bool MULTI>
 __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? 2 : 1)) void conv_pool_bf16(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, const float *__restrict__ cb,
