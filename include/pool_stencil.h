@@ -153,11 +153,13 @@ int ps_maxpool2d(const float *x, float *y, int N, int C, int H, int W, int k, in
  *   y  = 1 / (1 + exp(-(sm + bias2[co]) * scale))
  * x [N,Cin,H,W] float32, w [Cin,Cout,k,k] float32, convT_bias [Cout] float32 or NULL,
  * bias2 [Cout] float32, y [N,Cout,OH,OW] float32.
- * Supported: k = 4, stride = 2, pad = 1, dil = 1, output_padding in {0, 1},
- * Cout a multiple of 16 with 16 <= Cout <= 128, 1 <= Cin <= 256 where one parity
- * class's weights fit the LDS: (Cout*(16*Cq + 4) + 2*Cout)*4 <= 160 KB with
- * Cq = max(ceil(Cin/4), 6) (Cin <= 76 at Cout = 128); x with its channels rounded
- * up to 4*Cq, and y, below 2^29 elements each.  Beyond these PS_ERR_UNSUPPORTED. */
+ * Supported: k = 4, stride = 2, dil = 1, any pad >= 0 with OH, OW >= 1,
+ * output_padding in {0, 1}, Cout a multiple of 16 with 16 <= Cout <= 256, and
+ * 1 <= Cin <= 256 where one parity class's fp32 weights stay resident in the LDS
+ * of a compute unit: (Cout*(16*Cq + 4) + 2*Cout)*4 <= 160 KB with Cq = ceil(Cin/4)
+ * (Cin <= 76 at Cout = 128, <= 68 at 144, <= 36 at 256); x with its channels
+ * rounded up to 4*Cq, and y, below 2^29 elements each.  Beyond these
+ * PS_ERR_UNSUPPORTED. */
 int ps_convT_softmax_bias_scale_sigmoid(
     const float *x, const float *w, const float *convT_bias, const float *bias2, float *y,
     int N, int Cin, int H, int W, int Cout, int k, int stride, int pad, int output_padding,
@@ -167,10 +169,12 @@ int ps_convT_softmax_bias_scale_sigmoid(
  * products and accumulation, fp32 softmax and epilogue, y rounded to nearest even.
  * (The l2_p91 page considers reduced precision for this problem and keeps fp32;
  * this variant runs the GEMM on the bf16 matrix cores.)  convT_bias and bias2 are
- * float32.  Supported: k = 4, stride = 2, pad = 1, dil = 1, output_padding in
- * {0, 1}, Cout in {32, 64, 96, 128}, 2*Cout*(4*Cp + 8)*2 + 8*Cout <= 160 KB
- * with Cp = Cin rounded up to a multiple of 8 (Cout = 128) or 16 (else), i.e.
- * Cin <= 72 at Cout = 128, <= 144 at Cout = 64; and x below 2^30 elements. */
+ * float32.  Supported: k = 4, stride = 2, dil = 1, any pad >= 0 with OH, OW >= 1,
+ * output_padding in {0, 1}, Cout in {32, 64, 96, 128} (the bf16 kernels hold a
+ * pixel's channels for both column classes in one wave's registers), and
+ * 2*Cout*(4*Cp + 8)*2 + 8*Cout <= 160 KB with Cp = Cin rounded up to a multiple
+ * of 8 (Cout = 128) or 16 (else), i.e. Cin <= 72 at Cout = 128, <= 144 at
+ * Cout = 64; and x below 2^30 elements. */
 int ps_convT_softmax_bias_scale_sigmoid_bf16(
     const void *x, const void *w, const float *convT_bias, const float *bias2, void *y,
     int N, int Cin, int H, int W, int Cout, int k, int stride, int pad, int output_padding,
@@ -183,7 +187,7 @@ int ps_convT_softmax_bias_scale_sigmoid_bf16(
  *   y[n,co,oh,ow] = bias[co] + sum over (ci, ih, iw, kh, kw) with
  *                   oh = ih*s - p + kh*d, ow = iw*s - p + kw*d of x[n,ci,ih,iw]*w[ci,co,kh,kw]
  * x [N,Cin,H,W] float32, w [Cin,Cout,k,k] float32, bias [Cout] float32 or NULL,
- * y [N,Cout,OH,OW] float32.  Supported: the same set as the fused call above. */
+ * y [N,Cout,OH,OW] float32.  Supported: the same set as the fp32 fused call above. */
 int ps_convT2d(const float *x, const float *w, const float *bias, float *y, int N, int Cin, int H,
                int W, int Cout, int k, int stride, int pad, int output_padding, int dil,
                void *stream);

@@ -170,10 +170,10 @@ int ps_convT_softmax_bias_scale_sigmoid(const float *x, const float *w, const fl
     if (st != PS_OK) return st;
     if (too_big(N, Cin, H, W) || too_big(N, Cout, OH, OW) || too_big(Cin, Cout, k, k))
         return PS_ERR_SHAPE;
-    if (k != 4 || stride != 2 || pad != 1 || dil != 1) return PS_ERR_UNSUPPORTED;
-    if (Cout % 16 != 0 || Cout > 128 || Cin > 256) return PS_ERR_UNSUPPORTED;
+    if (k != 4 || stride != 2 || dil != 1) return PS_ERR_UNSUPPORTED;
+    if (Cout % 16 != 0 || Cout > 256 || Cin > 256) return PS_ERR_UNSUPPORTED;
     if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return PS_ERR_ALIGN;
-    return ps::launch_convT_softmax(x, w, convT_bias, bias2, y, N, Cin, H, W, Cout, OH, OW,
+    return ps::launch_convT_softmax(x, w, convT_bias, bias2, y, N, Cin, H, W, Cout, OH, OW, pad,
                                     scale, (hipStream_t)stream);
 }
 
@@ -191,7 +191,7 @@ int ps_convT_softmax_bias_scale_sigmoid_bf16(const void *x, const void *w,
     if (st != PS_OK) return st;
     if (too_big(N, Cin, H, W) || too_big(N, Cout, OH, OW) || too_big(Cin, Cout, k, k))
         return PS_ERR_SHAPE;
-    if (k != 4 || stride != 2 || pad != 1 || dil != 1) return PS_ERR_UNSUPPORTED;
+    if (k != 4 || stride != 2 || dil != 1) return PS_ERR_UNSUPPORTED;
     // both column classes' bf16 weights (2 x Cout x 4*Cin) must fit the LDS of a CU
     if (Cout % 32 != 0 || Cout > 128 ||
         (int64_t)2 * Cout * (4 * (Cout == 128 ? (Cin + 7) / 8 * 8 : (Cin + 15) / 16 * 16) + 8) *
@@ -199,8 +199,8 @@ int ps_convT_softmax_bias_scale_sigmoid_bf16(const void *x, const void *w,
         return PS_ERR_UNSUPPORTED;
     if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return PS_ERR_ALIGN;
     return ps::launch_convT_softmax_bf16((const uint16_t *)x, (const uint16_t *)w, convT_bias,
-                                         bias2, (uint16_t *)y, N, Cin, H, W, Cout, OH, OW, scale,
-                                         (hipStream_t)stream);
+                                         bias2, (uint16_t *)y, N, Cin, H, W, Cout, OH, OW, pad,
+                                         scale, (hipStream_t)stream);
 }
 
 int ps_convT2d(const float *x, const float *w, const float *bias, float *y, int N, int Cin, int H,
@@ -215,10 +215,10 @@ int ps_convT2d(const float *x, const float *w, const float *bias, float *y, int 
     if (st != PS_OK) return st;
     if (too_big(N, Cin, H, W) || too_big(N, Cout, OH, OW) || too_big(Cin, Cout, k, k))
         return PS_ERR_SHAPE;
-    if (k != 4 || stride != 2 || pad != 1 || dil != 1) return PS_ERR_UNSUPPORTED;
-    if (Cout % 16 != 0 || Cout > 128 || Cin > 256) return PS_ERR_UNSUPPORTED;
+    if (k != 4 || stride != 2 || dil != 1) return PS_ERR_UNSUPPORTED;
+    if (Cout % 16 != 0 || Cout > 256 || Cin > 256) return PS_ERR_UNSUPPORTED;
     if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return PS_ERR_ALIGN;
-    return ps::launch_convT(x, w, bias, y, N, Cin, H, W, Cout, OH, OW, (hipStream_t)stream);
+    return ps::launch_convT(x, w, bias, y, N, Cin, H, W, Cout, OH, OW, pad, (hipStream_t)stream);
 }
 
 int ps_tanh_scale_bias_maxpool(const void *y, const float *bias2, void *out, int dtype, int N,

@@ -518,9 +518,8 @@ int launch_t(const void *x, const void *w, const float *cb, const float *b2, voi
         hipFuncSetAttribute((const void *)conv_general<TI, EPI, PF>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
         return PS_ERR_HIP;
-    hipLaunchKernelGGL((conv_general<TI, EPI, PF>), dim3((unsigned)nblocks), dim3(kThreads),
-                       (size_t)lds, stream, (const TI *)x, (const TI *)w, cb, b2, (TI *)y, g);
-    return hipGetLastError() == hipSuccess ? PS_OK : PS_ERR_HIP;
+    return launch(conv_general<TI, EPI, PF>, dim3((unsigned)nblocks), dim3(kThreads),
+                  (size_t)lds, stream, (const TI *)x, (const TI *)w, cb, b2, (TI *)y, g);
 }
 
 template <typename TI, int EPI>

@@ -664,29 +664,25 @@ int launch_pk_npw(const void *x, const void *w, const float *cb, const float *b2
         const bool multi = Cout > 64;
         const dim3 grid((unsigned)nblocks), block(64 * NPW);
 #define PS_BF16_LAUNCH(V, M)                                                                  \
-    hipLaunchKernelGGL((conv_pool_bf16<PK, NPW, V, M>), grid, block, 0, stream,                \
-                       (const uint16_t *)x, (const uint16_t *)w, cb, b2, (uint16_t *)y, Cin, H, W, \
-                       Cout, pad, PH, PW, scale, npwt, (int)nseg)
-        if (vec && !multi) PS_BF16_LAUNCH(true, false);
-        else if (vec) PS_BF16_LAUNCH(true, true);
-        else if (!multi) PS_BF16_LAUNCH(false, false);
-        else PS_BF16_LAUNCH(false, true);
+    launch(conv_pool_bf16<PK, NPW, V, M>, grid, block, 0, stream, (const uint16_t *)x,        \
+           (const uint16_t *)w, cb, b2, (uint16_t *)y, Cin, H, W, Cout, pad, PH, PW, scale,   \
+           npwt, (int)nseg)
+        if (vec && !multi) return PS_BF16_LAUNCH(true, false);
+        if (vec) return PS_BF16_LAUNCH(true, true);
+        if (!multi) return PS_BF16_LAUNCH(false, false);
+        return PS_BF16_LAUNCH(false, true);
 #undef PS_BF16_LAUNCH
-        return hipGetLastError() == hipSuccess ? PS_OK : PS_ERR_HIP;
     }
     const uint64_t nblocks = (uint64_t)N * PH * npwt;
     if (nblocks > 0x7fffffffull) return PS_ERR_UNSUPPORTED;
     const dim3 grid((unsigned)nblocks), block(64 * NPW);
-    if (Cin <= 4) {
-        hipLaunchKernelGGL((conv_pool_f32<PK, NPW, 1>), grid, block, 0, stream, (const float *)x,
-                           (const float *)w, cb, b2, (float *)y, Cin, H, W, Cout, pad, PH, PW,
-                           scale, npwt);
-    } else {
-        hipLaunchKernelGGL((conv_pool_f32<PK, NPW, 2>), grid, block, 0, stream, (const float *)x,
-                           (const float *)w, cb, b2, (float *)y, Cin, H, W, Cout, pad, PH, PW,
-                           scale, npwt);
-    }
-    return hipGetLastError() == hipSuccess ? PS_OK : PS_ERR_HIP;
+    if (Cin <= 4)
+        return launch(conv_pool_f32<PK, NPW, 1>, grid, block, 0, stream, (const float *)x,
+                      (const float *)w, cb, b2, (float *)y, Cin, H, W, Cout, pad, PH, PW, scale,
+                      npwt);
+    return launch(conv_pool_f32<PK, NPW, 2>, grid, block, 0, stream, (const float *)x,
+                  (const float *)w, cb, b2, (float *)y, Cin, H, W, Cout, pad, PH, PW, scale,
+                  npwt);
 }
 
 template <int PK>

@@ -1,15 +1,17 @@
-// Fused ConvTranspose2d(k4, s2, p1) -> softmax over channels -> +bias2 -> *scale -> sigmoid
-// for gfx950.
+// Fused ConvTranspose2d(k4, s2, any padding p) -> softmax over channels -> +bias2 -> *scale
+// -> sigmoid for gfx950.
 //
 // Definition (POPCORNBENCH page Kimi-K2.6 l2_p91, problem statement and its
 // scatter loop):
-//   t[n,co,oh,ow] = bias[co] + sum over (ci, ih, iw, kh, kw) with oh = 2*ih - 1 + kh,
-//                   ow = 2*iw - 1 + kw of x[n,ci,ih,iw] * w[ci,co,kh,kw]
+//   t[n,co,oh,ow] = bias[co] + sum over (ci, ih, iw, kh, kw) with oh = 2*ih - p + kh,
+//                   ow = 2*iw - p + kw of x[n,ci,ih,iw] * w[ci,co,kh,kw]
 //   y = sigmoid((softmax_co(t) + bias2[co]) * scale)
 //
-// Parity decomposition (the page's phase table): output row oh = 2m + a only
-// receives kernel rows kh = 1 - a + 2u (u = 0, 1), from input rows
-// ih = m + a - u; columns likewise with (b, v).  Each of the four classes
+// Parity decomposition (the page's phase table, written there for p = 1): output
+// row oh = 2m + a only receives the kernel rows of one parity, kh = ka + 2u
+// (u = 0, 1) with ka = (a + p) mod 2, from input rows ih = m + ra - u with
+// ra = floor((a + p) / 2) (2*ih + kh = oh + p); for p = 1 that is kh = 1 - a + 2u
+// from ih = m + a - u.  Columns likewise with (b, v).  Each of the four classes
 // (a, b) is therefore a dense GEMM
 //   D[co][pixel] = sum_{k = (ci, u, v)} A_ab[co][k] * B_ab[k][pixel],  K = 4*Cin,
 // with a class-specific weight matrix A_ab (a 2x2 sub-kernel per (ci, co)).
@@ -67,7 +69,7 @@ template <int MT, int NQ, bool SOFTMAX>
 __global__ __launch_bounds__(kThreads) void convT_softmax_f32(
     const float *__restrict__ x, const float *__restrict__ w, const float *__restrict__ cbias,
     const float *__restrict__ b2, float *__restrict__ y, int N, int Cin, int H, int W, int OH,
-    int OW, float scale, int Cq, ClassGeom geo) {
+    int OW, int pad, float scale, int Cq, ClassGeom geo) {
     constexpr int COUT = 16 * MT;
     extern __shared__ float lds[];
     const int KS = 4 * Cq;          // K-steps per lane group
@@ -85,8 +87,11 @@ __global__ __launch_bounds__(kThreads) void convT_softmax_f32(
     const int wg_per_class = geo.start[cls + 1] - geo.start[cls];
     const uint32_t Mc = geo.Mc[a], mM = geo.mM[a];  // rows of this class
     const uint32_t Qc = geo.Qc[b], mQ = geo.mQ[b];  // columns of this class
+    // kernel row / column of tap u = 0 / v = 0, and the input row / column offsets
+    const int ka = (a + pad) & 1, ra = (a + pad) >> 1;
+    const int kb = (b + pad) & 1, rb = (b + pad) >> 1;
 
-    // ---- stage A_ab: lw[co][G][s] = w[ci][co][1-a+2u][1-b+2v],
+    // ---- stage A_ab: lw[co][G][s] = w[ci][co][ka+2u][kb+2v],
     //      ci = G*Cq + s/4, (u, v) = ((s%4)/2, (s%4)%2); zero for ci >= Cin
     for (int e = threadIdx.x; e < COUT * 4 * KS; e += kThreads) {
         const int s = e % KS;
@@ -94,7 +99,7 @@ __global__ __launch_bounds__(kThreads) void convT_softmax_f32(
         const int co = e / (4 * KS);
         const int ci = G * Cq + (s >> 2);
         const int u = (s >> 1) & 1, v = s & 1;
-        const int kh = 1 - a + 2 * u, kw = 1 - b + 2 * v;
+        const int kh = ka + 2 * u, kw = kb + 2 * v;
         float val = 0.f;
         if (ci < Cin) val = w[(((size_t)ci * COUT + co) * 4 + kh) * 4 + kw];
         lw[co * CS + G * KS + s] = val;
@@ -144,7 +149,7 @@ __global__ __launch_bounds__(kThreads) void convT_softmax_f32(
             const uint32_t q = Pc - t * Qc;
             const uint32_t n = fdiv(t, mM);
             const uint32_t m = t - n * Mc;
-            const int ih0 = (int)m + a, iw0 = (int)q + b;  // u = 0 / v = 0 input position
+            const int ih0 = (int)m + ra, iw0 = (int)q + rb;  // u = 0 / v = 0 input position
             const bool r0 = ih0 < H, r1 = ih0 >= 1 && ih0 - 1 < H;
             const bool c0 = iw0 < W, c1 = iw0 >= 1 && iw0 - 1 < W;
             const uint32_t o = 4u * ((n * Cin + G * Cq) * plane + (uint32_t)ih0 * W + iw0);
@@ -308,8 +313,11 @@ __global__ __launch_bounds__(kThreads) void convT_softmax_f32(
 
 template <int MT, bool SOFTMAX>
 int launch_mt(const float *x, const float *w, const float *cb, const float *b2, float *y, int N,
-              int Cin, int H, int W, int OH, int OW, float scale, hipStream_t stream) {
-    constexpr int NQ = 2;
+              int Cin, int H, int W, int OH, int OW, int pad, float scale, hipStream_t stream) {
+    // pixel groups per wave tile: two (32 pixels) up to 128 channels; one beyond, so
+    // that accumulators (4*MT*NQ) and A operands (4*MT) stay within the registers of
+    // two waves per SIMD
+    constexpr int NQ = MT > 8 ? 1 : 2;
     const int Cq = (Cin + 3) / 4;
     const int KS = 4 * Cq;
     const size_t lds_bytes = ((size_t)16 * MT * (4 * KS + 4) + 2 * 16 * MT) * sizeof(float);
@@ -372,25 +380,23 @@ int launch_mt(const float *x, const float *w, const float *cb, const float *b2, 
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes) !=
             hipSuccess)
         return PS_ERR_HIP;
-    hipLaunchKernelGGL((convT_softmax_f32<MT, NQ, SOFTMAX>), dim3(nblocks), dim3(kThreads),
-                       lds_bytes, stream, x, w, cb, b2, y, N, Cin, H, W, OH, OW, scale, Cq, geo);
-    return hipGetLastError() == hipSuccess ? PS_OK : PS_ERR_HIP;
+    return launch(convT_softmax_f32<MT, NQ, SOFTMAX>, dim3(nblocks), dim3(kThreads), lds_bytes,
+                  stream, x, w, cb, b2, y, N, Cin, H, W, OH, OW, pad, scale, Cq, geo);
 }
 
 template <bool SOFTMAX>
 int launch_cout(const float *x, const float *w, const float *cb, const float *b2, float *y, int N,
-                int Cin, int H, int W, int Cout, int OH, int OW, float scale,
+                int Cin, int H, int W, int Cout, int OH, int OW, int pad, float scale,
                 hipStream_t stream) {
+#define PS_CONVT_MT(M) \
+    case M: return launch_mt<M, SOFTMAX>(x, w, cb, b2, y, N, Cin, H, W, OH, OW, pad, scale, stream)
     switch (Cout / 16) {
-        case 1: return launch_mt<1, SOFTMAX>(x, w, cb, b2, y, N, Cin, H, W, OH, OW, scale, stream);
-        case 2: return launch_mt<2, SOFTMAX>(x, w, cb, b2, y, N, Cin, H, W, OH, OW, scale, stream);
-        case 3: return launch_mt<3, SOFTMAX>(x, w, cb, b2, y, N, Cin, H, W, OH, OW, scale, stream);
-        case 4: return launch_mt<4, SOFTMAX>(x, w, cb, b2, y, N, Cin, H, W, OH, OW, scale, stream);
-        case 5: return launch_mt<5, SOFTMAX>(x, w, cb, b2, y, N, Cin, H, W, OH, OW, scale, stream);
-        case 6: return launch_mt<6, SOFTMAX>(x, w, cb, b2, y, N, Cin, H, W, OH, OW, scale, stream);
-        case 7: return launch_mt<7, SOFTMAX>(x, w, cb, b2, y, N, Cin, H, W, OH, OW, scale, stream);
-        case 8: return launch_mt<8, SOFTMAX>(x, w, cb, b2, y, N, Cin, H, W, OH, OW, scale, stream);
+        PS_CONVT_MT(1); PS_CONVT_MT(2); PS_CONVT_MT(3); PS_CONVT_MT(4);
+        PS_CONVT_MT(5); PS_CONVT_MT(6); PS_CONVT_MT(7); PS_CONVT_MT(8);
+        PS_CONVT_MT(9); PS_CONVT_MT(10); PS_CONVT_MT(11); PS_CONVT_MT(12);
+        PS_CONVT_MT(13); PS_CONVT_MT(14); PS_CONVT_MT(15); PS_CONVT_MT(16);
     }
+#undef PS_CONVT_MT
     return PS_ERR_UNSUPPORTED;
 }
 
@@ -398,14 +404,14 @@ int launch_cout(const float *x, const float *w, const float *cb, const float *b2
 
 int launch_convT_softmax(const float *x, const float *w, const float *convT_bias,
                          const float *bias2, float *y, int N, int Cin, int H, int W, int Cout,
-                         int OH, int OW, float scale, hipStream_t stream) {
-    return launch_cout<true>(x, w, convT_bias, bias2, y, N, Cin, H, W, Cout, OH, OW, scale,
+                         int OH, int OW, int pad, float scale, hipStream_t stream) {
+    return launch_cout<true>(x, w, convT_bias, bias2, y, N, Cin, H, W, Cout, OH, OW, pad, scale,
                              stream);
 }
 
 int launch_convT(const float *x, const float *w, const float *convT_bias, float *y, int N,
-                 int Cin, int H, int W, int Cout, int OH, int OW, hipStream_t stream) {
-    return launch_cout<false>(x, w, convT_bias, nullptr, y, N, Cin, H, W, Cout, OH, OW, 1.f,
+                 int Cin, int H, int W, int Cout, int OH, int OW, int pad, hipStream_t stream) {
+    return launch_cout<false>(x, w, convT_bias, nullptr, y, N, Cin, H, W, Cout, OH, OW, pad, 1.f,
                               stream);
 }
 

@@ -1,11 +1,13 @@
-// bf16 ConvTranspose2d(k4, s2, p1) -> softmax over channels -> +bias2 -> *scale
-// -> sigmoid for gfx950: bf16 x, w and output, fp32 accumulation.
+// bf16 ConvTranspose2d(k4, s2, any padding p) -> softmax over channels -> +bias2
+// -> *scale -> sigmoid for gfx950: bf16 x, w and output, fp32 accumulation.
 //
 // Same definition and parity decomposition as the fp32 kernel (POPCORNBENCH
 // page Kimi-K2.6 l2_p91: problem statement, scatter loop and phase table):
 // output row oh = 2m + a, column ow = 2q + b receives kernel taps
-// kh = 1 - a + 2u, kw = 1 - b + 2v from input (m + a - u, q + b - v), so each
-// parity class (a, b) is a dense GEMM with K = 4*Cin, k = 4*ci + (2u + v).
+// kh = ka + 2u, kw = kb + 2v from input (m + ra - u, q + rb - v), with
+// ka = (a + p) mod 2, ra = floor((a + p) / 2) and likewise kb, rb (for p = 1:
+// kh = 1 - a + 2u from row m + a - u), so each parity class (a, b) is a dense
+// GEMM with K = 4*Cin, k = 4*ci + (2u + v).
 // The page weighs reduced precision for this problem and keeps fp32; this
 // variant takes bf16 operands (products exact in fp32) for the bf16 matrix
 // cores.
@@ -49,7 +51,8 @@ template <int MT>  // Cout = 32 * MT
 __global__ __launch_bounds__(kThreads, 1) void convT_softmax_bf16(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
     const float *__restrict__ cbias, const float *__restrict__ b2, uint16_t *__restrict__ y,
-    int N, int Cin, int H, int W, int OH, int OW, float scale, int C4, int wg_per_class) {
+    int N, int Cin, int H, int W, int OH, int OW, int pad, float scale, int C4,
+    int wg_per_class) {
     constexpr int COUT = 32 * MT;
     constexpr int kRing = ring_steps<MT>();
     extern __shared__ float lds[];
@@ -65,13 +68,14 @@ __global__ __launch_bounds__(kThreads, 1) void convT_softmax_bf16(
     const int a = (blk >> 3) & 1;
     const int rank = (blk & 7) + 8 * (blk >> 4);
     const int Mc = (OH - a + 1) >> 1;        // output rows of this row class
+    const int ka = (a + pad) & 1, ra = (a + pad) >> 1;
 
     for (int e = threadIdx.x; e < 2 * COUT * K; e += kThreads) {
         const int k = e % K;
         const int rest = e / K;
         const int co = rest % COUT, b = rest / COUT;
         const int ci = k >> 2, u = (k >> 1) & 1, v = k & 1;
-        const int kh = 1 - a + 2 * u, kw = 1 - b + 2 * v;
+        const int kh = ka + 2 * u, kw = ((b + pad) & 1) + 2 * v;
         la[(b * COUT + co) * KP + k] = ci < Cin ? w[(((size_t)ci * COUT + co) * 4 + kh) * 4 + kw] : 0;
     }
     for (int e = threadIdx.x; e < COUT; e += kThreads) {
@@ -108,7 +112,7 @@ __global__ __launch_bounds__(kThreads, 1) void convT_softmax_bf16(
         const int q = Pc % Qmax;
         const int m = (Pc / Qmax) % Mc;
         const int n = Pc / (Qmax * Mc);
-        const int ih0 = m + a;                // input row of tap u = 0
+        const int ih0 = m + ra;               // input row of tap u = 0
         const bool r0 = ih0 < H, r1 = ih0 >= 1 && ih0 - 1 < H;
         const uint32_t xrow = (uint32_t)((n * Cin + 2 * h) * plane + ih0 * W);
         const uint32_t yrow = (uint32_t)(n * COUT * oplane + (2 * m + a) * OW);
@@ -117,7 +121,7 @@ __global__ __launch_bounds__(kThreads, 1) void convT_softmax_bf16(
         for (int b = 0; b < 2; ++b) {
             const int Qc = (OW - b + 1) >> 1;
             const bool pok = inr && q < Qc;
-            const int iw0 = q + b;            // input column of tap v = 0
+            const int iw0 = q + ((b + pad) >> 1);  // input column of tap v = 0
             const bool c0 = iw0 < W, c1 = iw0 >= 1 && iw0 - 1 < W;
             const bool m00 = pok && r0 && c0, m01 = pok && r0 && c1;
             const bool m10 = pok && r1 && c0, m11 = pok && r1 && c1;
@@ -237,22 +241,23 @@ __global__ __launch_bounds__(kThreads, 1) void convT_softmax_bf16(
 // ---------------------------------------------------------------------------------
 // Staged variant, taken when W % 8 == 0 and its buffers fit the LDS.
 //
-// Indexing the pixels of a row class by input position instead: output (oh, ow) =
-// (2r - a, 2c - b) takes input rows r - u and columns c - v (u, v in {0, 1}) with
-// kernel taps kh = 1 - a + 2u, kw = 1 - b + 2v, so the B operand of position (r, c)
-// is the same for both column classes b and one B fragment feeds the MFMAs of both
-// (positions c = 0 .. W cover every output column; ow outside [0, OW) is masked).
+// Indexing the pixels of a row class by input position instead: output row 2m + a
+// takes input rows r - u with r = m + ra, and output column 2c - p + (b ^ (p mod 2))
+// takes input columns c - v (u, v in {0, 1}) with kernel taps kh = ka + 2u,
+// kw = kb + 2v, so the B operand of position (r, c) is the same for both column
+// classes b and one B fragment feeds the MFMAs of both (positions c = floor(p/2) ..
+// floor((OW - 1 + p)/2) cover every output column; ow outside [0, OW) is masked).
 //
 // Input channels are staged 8 at a time in LDS, channel-last: [slot][col + 1][8
-// channels], 16 bytes per entry, with zero entries at columns -1 and W, so a lane's B
+// channels], 16 bytes per entry, with zero entries at columns -1, W and W + 1, so a lane's B
 // fragment (8 channels of one tap) is one 16-byte LDS read.  The global reads that
 // fill a chunk are 16 bytes wide (8 columns of one channel) and are issued one chunk
 // ahead; a thread transposes two channels x 8 columns with byte permutes into 8
 // 4-byte LDS writes.  K order: k = 32*(ci/8) + 8*(2u + v) + ci%8; K-step s = (chunk
 // ci/8, u), lane half h holding tap v = h.
 //
-// Work item: 256 consecutive positions p = m*(W + 1) + c of one image and row class
-// (8 waves x 32), which touch at most `slots` input rows.
+// Work item: 256 consecutive positions m*Wc + (c - cmin) of one image and row class
+// (8 waves x 32, Wc positions per row), which touch at most `slots` input rows.
 constexpr int kStagedPix = 256;
 constexpr int kStageRow = 66;  // bf16 per row of a wave's output staging (64 + pad)
 
@@ -262,7 +267,7 @@ template <int MT>  // Cout = 32 * MT
 __global__ __launch_bounds__(kThreads, 1) void convT_softmax_bf16_staged(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
     const float *__restrict__ cbias, const float *__restrict__ b2, uint16_t *__restrict__ y,
-    int N, int Cin, int H, int W, int OH, int OW, float scale, int C8, int slots,
+    int N, int Cin, int H, int W, int OH, int OW, int pad, float scale, int C8, int slots,
     int wg_per_class) {
     constexpr int COUT = 32 * MT;
     extern __shared__ float lds[];
@@ -271,8 +276,8 @@ __global__ __launch_bounds__(kThreads, 1) void convT_softmax_bf16_staged(
     uint16_t *la = (uint16_t *)lds;               // [b][COUT][KP]
     float *lcb = lds + COUT * KP;                 // conv-transpose bias * log2e
     float *lb2 = lcb + COUT;                      // -bias2 * scale * log2e
-    uint4 *lx = (uint4 *)(lb2 + COUT);            // [2][slots][W + 2] input entries
-    const int WE = W + 2;
+    uint4 *lx = (uint4 *)(lb2 + COUT);            // [2][slots][W + 3] input entries
+    const int WE = W + 3;                         // input columns -1 .. W + 1
     const int bufsz = slots * WE;
     // per wave: 8 channels x 64 output columns of bf16 outputs on their way to memory
     uint16_t *lo = (uint16_t *)(lx + 2 * bufsz) + (threadIdx.x >> 6) * 8 * kStageRow;
@@ -280,8 +285,12 @@ __global__ __launch_bounds__(kThreads, 1) void convT_softmax_bf16_staged(
     const int blk = blockIdx.x;
     const int a = (blk >> 3) & 1;
     const int rank = (blk & 7) + 8 * (blk >> 4);
-    const int Mc = (OH - a + 1) >> 1;             // rows r = m + a of this row class
-    const int Wc = W + 1;                         // positions c = 0 .. W
+    const int Mc = (OH - a + 1) >> 1;             // output rows 2m + a of this row class
+    const int ka = (a + pad) & 1, ra = (a + pad) >> 1;  // input row m + ra - u, tap ka + 2u
+    // Positions: input columns c = cmin .. cmax (tap v = 0); class b writes output column
+    // 2c - pad + (b ^ (pad & 1)), so these positions cover every output column.
+    const int cmin = pad >> 1;
+    const int Wc = ((OW - 1 + pad) >> 1) - cmin + 1;
     const int npix = Mc * Wc;
     const int ipi = (npix + kStagedPix - 1) / kStagedPix;  // items per image
     const int nitems = N * ipi;
@@ -293,7 +302,7 @@ __global__ __launch_bounds__(kThreads, 1) void convT_softmax_bf16_staged(
         const int co = rest % COUT, b = rest / COUT;
         const int ci = 8 * (k >> 5) + (k & 7);
         const int t = (k >> 3) & 3;
-        const int kh = 1 - a + 2 * (t >> 1), kw = 1 - b + 2 * (t & 1);
+        const int kh = ka + 2 * (t >> 1), kw = ((b + pad) & 1) + 2 * (t & 1);
         la[(b * COUT + co) * KP + k] = ci < Cin ? w[(((size_t)ci * COUT + co) * 4 + kh) * 4 + kw] : 0;
     }
     for (int e = threadIdx.x; e < COUT; e += kThreads) {
@@ -303,6 +312,7 @@ __global__ __launch_bounds__(kThreads, 1) void convT_softmax_bf16_staged(
     for (int e = threadIdx.x; e < 2 * slots; e += kThreads) {
         lx[e * WE] = make_uint4(0u, 0u, 0u, 0u);
         lx[e * WE + W + 1] = make_uint4(0u, 0u, 0u, 0u);
+        lx[e * WE + W + 2] = make_uint4(0u, 0u, 0u, 0u);
     }
 
     // ---- chunk fill: thread -> (slot, 8-column group g, channel pair cp) ----
@@ -317,7 +327,7 @@ __global__ __launch_bounds__(kThreads, 1) void convT_softmax_bf16_staged(
     auto fill_load = [&](int it, int k, uint32_t (&v)[8]) {
         const int n = it / ipi;
         const int m0 = ((it - n * ipi) * kStagedPix) / Wc;
-        const int ir = m0 + a - 1 + f_slot;
+        const int ir = m0 + ra - 1 + f_slot;
         const int ch = 8 * k + 2 * f_cp;
         const bool rok = f_on && ir >= 0 && ir < H;
         const uint32_t o = 2u * (((uint32_t)(n * Cin + ch) * (uint32_t)H + (uint32_t)ir) * (uint32_t)W +
@@ -363,8 +373,8 @@ __global__ __launch_bounds__(kThreads, 1) void convT_softmax_bf16_staged(
         const int pc = pv ? p : p0;
         const int m = pc / Wc;
         const int c = pc - m * Wc;
-        // B entries of taps (u, v = h), u = 0, 1: input (m + a - u, c - h)
-        const int eo0 = (m - m0 + 1) * WE + (c - h + 1);
+        // B entries of taps (u, v = h), u = 0, 1: input (m + ra - u, cmin + c - h)
+        const int eo0 = (m - m0 + 1) * WE + (cmin + c - h + 1);
         const int eo1 = eo0 - WE;
         const uint16_t *ab = la + j * KP + 8 * h;
 
@@ -431,17 +441,18 @@ __global__ __launch_bounds__(kThreads, 1) void convT_softmax_bf16_staged(
             inv[b] = ninv_s * __builtin_amdgcn_rcpf(sum);
         }
         // The 32 positions x 2 column classes of the wave are 64 output columns
-        // ow = 2c - b, ascending within an output row: slot 2j + 1 - b.  Each 8-channel
-        // group goes through LDS so that a store writes one channel's 64 columns (128
-        // contiguous bytes, or two runs where the positions wrap to the next row).
-        // Store lane L takes slot L: position L/2, class 1 - L%2; a masked store gets
-        // an offset past the end of the range (dropped).
+        // ow = 2c - pad + (b ^ podd), ascending within an output row: slot 2j + (b ^ podd).
+        // Each 8-channel group goes through LDS so that a store writes one channel's 64
+        // columns (128 contiguous bytes, or two runs where the positions wrap to the next
+        // row).  Store lane L takes slot L: position L/2, output column 2c - pad + L%2; a
+        // masked store gets an offset past the end of the range (dropped).
+        const int podd = pad & 1;
         const __amdgpu_buffer_rsrc_t yr =
             make_range_checked(y + (size_t)n * COUT * oplane, ybytes);
         const int ps = p0 + 32 * wv + (lane >> 1);
         const bool psv = ps < npix;
         const int msx = psv ? ps / Wc : 0;
-        const int ows = 2 * (psv ? ps - msx * Wc : 0) - (1 - (lane & 1));
+        const int ows = 2 * (cmin + (psv ? ps - msx * Wc : 0)) - pad + (lane & 1);
         const uint32_t so = (psv && ows >= 0 && ows < OW)
                                 ? 2u * (uint32_t)((2 * msx + a) * OW + ows)
                                 : 0x80000000u;
@@ -458,7 +469,7 @@ __global__ __launch_bounds__(kThreads, 1) void convT_softmax_bf16_staged(
                     for (int r = 0; r < 4; ++r) {
                         const float t =
                             __builtin_amdgcn_exp2f(fmaf(acc[b][mt][4 * i4 + r], inv[b], bv[r]));
-                        lo[(4 * h + r) * kStageRow + 2 * j + 1 - b] =
+                        lo[(4 * h + r) * kStageRow + 2 * j + (b ^ podd)] =
                             f32_to_bf16_rne(__builtin_amdgcn_rcpf(1.f + t));
                     }
 #pragma unroll
@@ -472,7 +483,8 @@ __global__ __launch_bounds__(kThreads, 1) void convT_softmax_bf16_staged(
 
 template <int MT>
 int launch_mt(const uint16_t *x, const uint16_t *w, const float *cb, const float *b2, uint16_t *y,
-              int N, int Cin, int H, int W, int OH, int OW, float scale, hipStream_t stream) {
+              int N, int Cin, int H, int W, int OH, int OW, int pad, float scale,
+              hipStream_t stream) {
     constexpr int kRing = ring_steps<MT>();
     const int C4 = (Cin + 4 * kRing - 1) / (4 * kRing) * (4 * kRing);  // whole rings of K-steps
     const int KP = 4 * C4 + 8;
@@ -494,10 +506,10 @@ int launch_mt(const uint16_t *x, const uint16_t *w, const float *cb, const float
     // and masked output offsets (2^31 + image bytes) that cannot wrap
     {
         const int C8 = (Cin + 7) / 8 * 8;
-        const int Wc = W + 1;
+        const int Wc = ((OW - 1 + pad) >> 1) - (pad >> 1) + 1;   // positions per row
         const int slots = (Wc + kStagedPix - 2) / Wc + 2;
         const size_t lds_staged = (size_t)2 * 32 * MT * (4 * C8 + 8) * 2 +
-                                  2 * 32 * MT * sizeof(float) + (size_t)2 * slots * (W + 2) * 16 +
+                                  2 * 32 * MT * sizeof(float) + (size_t)2 * slots * (W + 3) * 16 +
                                   (size_t)(kThreads / 64) * 8 * kStageRow * 2;
         if (W % 8 == 0 && (int64_t)slots * (W / 8) * 4 <= kThreads &&
             lds_staged <= 160 * 1024 && (int64_t)2 * 32 * MT * OH * OW < (1ll << 31)) {
@@ -506,10 +518,9 @@ int launch_mt(const uint16_t *x, const uint16_t *w, const float *cb, const float
                                     hipFuncAttributeMaxDynamicSharedMemorySize,
                                     (int)lds_staged) != hipSuccess)
                 return PS_ERR_HIP;
-            hipLaunchKernelGGL((convT_softmax_bf16_staged<MT>), dim3(nblocks), dim3(kThreads),
-                               lds_staged, stream, x, w, cb, b2, y, N, Cin, H, W, OH, OW, scale,
-                               C8, slots, wg_per_class);
-            return hipGetLastError() == hipSuccess ? PS_OK : PS_ERR_HIP;
+            return launch(convT_softmax_bf16_staged<MT>, dim3(nblocks), dim3(kThreads),
+                          lds_staged, stream, x, w, cb, b2, y, N, Cin, H, W, OH, OW, pad, scale,
+                          C8, slots, wg_per_class);
         }
     }
 
@@ -518,21 +529,20 @@ int launch_mt(const uint16_t *x, const uint16_t *w, const float *cb, const float
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes) !=
             hipSuccess)
         return PS_ERR_HIP;
-    hipLaunchKernelGGL((convT_softmax_bf16<MT>), dim3(nblocks), dim3(kThreads), lds_bytes, stream,
-                       x, w, cb, b2, y, N, Cin, H, W, OH, OW, scale, C4, wg_per_class);
-    return hipGetLastError() == hipSuccess ? PS_OK : PS_ERR_HIP;
+    return launch(convT_softmax_bf16<MT>, dim3(nblocks), dim3(kThreads), lds_bytes, stream, x, w,
+                  cb, b2, y, N, Cin, H, W, OH, OW, pad, scale, C4, wg_per_class);
 }
 
 }  // namespace
 
 int launch_convT_softmax_bf16(const uint16_t *x, const uint16_t *w, const float *convT_bias,
                               const float *bias2, uint16_t *y, int N, int Cin, int H, int W,
-                              int Cout, int OH, int OW, float scale, hipStream_t stream) {
+                              int Cout, int OH, int OW, int pad, float scale, hipStream_t stream) {
     switch (Cout / 32) {
-        case 1: return launch_mt<1>(x, w, convT_bias, bias2, y, N, Cin, H, W, OH, OW, scale, stream);
-        case 2: return launch_mt<2>(x, w, convT_bias, bias2, y, N, Cin, H, W, OH, OW, scale, stream);
-        case 3: return launch_mt<3>(x, w, convT_bias, bias2, y, N, Cin, H, W, OH, OW, scale, stream);
-        case 4: return launch_mt<4>(x, w, convT_bias, bias2, y, N, Cin, H, W, OH, OW, scale, stream);
+        case 1: return launch_mt<1>(x, w, convT_bias, bias2, y, N, Cin, H, W, OH, OW, pad, scale, stream);
+        case 2: return launch_mt<2>(x, w, convT_bias, bias2, y, N, Cin, H, W, OH, OW, pad, scale, stream);
+        case 3: return launch_mt<3>(x, w, convT_bias, bias2, y, N, Cin, H, W, OH, OW, pad, scale, stream);
+        case 4: return launch_mt<4>(x, w, convT_bias, bias2, y, N, Cin, H, W, OH, OW, pad, scale, stream);
     }
     return PS_ERR_UNSUPPORTED;
 }

@@ -452,10 +452,9 @@ int launch_rows_sd_v(const float *x, float *y, int N, int C, int H, int W, int O
         hipFuncSetAttribute((const void *)maxpool_rows_sd<K, S, D, V, PS_MPSD_PF, EPI>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes) != hipSuccess)
         return PS_ERR_HIP;
-    hipLaunchKernelGGL((maxpool_rows_sd<K, S, D, V, PS_MPSD_PF, EPI>), dim3((unsigned)nblocks),
-                       dim3(256), lds_bytes, stream, x, y, H, W, OH, OW, p, band_rows, nbands,
-                       nstrips, ntasks, epi);
-    return hipGetLastError() == hipSuccess ? PS_OK : PS_ERR_HIP;
+    return launch(maxpool_rows_sd<K, S, D, V, PS_MPSD_PF, EPI>, dim3((unsigned)nblocks),
+                  dim3(256), lds_bytes, stream, x, y, H, W, OH, OW, p, band_rows, nbands, nstrips,
+                  ntasks, epi);
 }
 
 // strips of 64 output columns for rows up to 64 wide (no idle chunks), else 256
@@ -592,10 +591,9 @@ int launch_rows(const float *x, float *y, int N, int C, int H, int W, int OH, in
         hipFuncSetAttribute((const void *)maxpool_s1_rows<K, V, PS_MAXPOOL_PREFETCH>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes) != hipSuccess)
         return PS_ERR_HIP;
-    hipLaunchKernelGGL((maxpool_s1_rows<K, V, PS_MAXPOOL_PREFETCH>), dim3((unsigned)nblocks), dim3(kWave * nw),
-                       lds_bytes, stream,
-                       x, y, H, W, OH, OW, p, band_rows, nbands, nstrips, ntasks);
-    return hipGetLastError() == hipSuccess ? PS_OK : PS_ERR_HIP;
+    return launch(maxpool_s1_rows<K, V, PS_MAXPOOL_PREFETCH>, dim3((unsigned)nblocks),
+                  dim3(kWave * nw), lds_bytes, stream, x, y, H, W, OH, OW, p, band_rows, nbands,
+                  nstrips, ntasks);
 }
 
 template <int K>
@@ -639,27 +637,22 @@ int launch_maxpool2d(const float *x, float *y, int N, int C, int H, int W, int O
     if (grid.y > 65535u) return PS_ERR_UNSUPPORTED;
     const int pl = (int)planes;
 #define PS_COLS(KC)                                                                            \
-    do {                                                                                       \
-        if (rb == 8)                                                                           \
-            hipLaunchKernelGGL((maxpool_cols<KC, 8>), grid, dim3(256), 0, stream, x, y, H, W, \
-                               OH, OW, k, s, p, d, pl);                                        \
-        else                                                                                   \
-            hipLaunchKernelGGL((maxpool_cols<KC, 1>), grid, dim3(256), 0, stream, x, y, H, W, \
-                               OH, OW, k, s, p, d, pl);                                        \
-    } while (0)
+    return rb == 8 ? launch(maxpool_cols<KC, 8>, grid, dim3(256), 0, stream, x, y, H, W, OH, OW, \
+                            k, s, p, d, pl)                                                      \
+                   : launch(maxpool_cols<KC, 1>, grid, dim3(256), 0, stream, x, y, H, W, OH, OW, \
+                            k, s, p, d, pl)
     switch (k) {
-        case 1: PS_COLS(1); break;
-        case 2: PS_COLS(2); break;
-        case 3: PS_COLS(3); break;
-        case 4: PS_COLS(4); break;
-        case 5: PS_COLS(5); break;
-        case 6: PS_COLS(6); break;
-        case 7: PS_COLS(7); break;
-        case 8: PS_COLS(8); break;
-        default: PS_COLS(0); break;
+        case 1: PS_COLS(1);
+        case 2: PS_COLS(2);
+        case 3: PS_COLS(3);
+        case 4: PS_COLS(4);
+        case 5: PS_COLS(5);
+        case 6: PS_COLS(6);
+        case 7: PS_COLS(7);
+        case 8: PS_COLS(8);
+        default: PS_COLS(0);
     }
 #undef PS_COLS
-    return hipGetLastError() == hipSuccess ? PS_OK : PS_ERR_HIP;
 }
 
 // The fp32 tanh -> *scale -> +bias2 -> max-pool stage through the streaming kernel;

@@ -5,9 +5,29 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <tuple>
+
 #include "pool_stencil.h"
 
 namespace ps {
+
+// Enqueue a kernel and return the status of THIS launch: hipLaunchKernel reports
+// the launch's own error, so an earlier, unrelated sticky error on the calling
+// thread is neither taken for this call's failure nor cleared.  The arguments are
+// converted to the kernel's parameter types first (as a <<<>>> launch would).
+template <typename... KArgs, typename... Args>
+int launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t shmem, hipStream_t stream,
+           Args... args) {
+    static_assert(sizeof...(KArgs) == sizeof...(Args), "kernel argument count");
+    std::tuple<KArgs...> params(static_cast<KArgs>(args)...);
+    const hipError_t st = std::apply(
+        [&](auto &...p) {
+            void *ptrs[] = {(void *)&p...};
+            return hipLaunchKernel((const void *)kernel, grid, block, ptrs, shmem, stream);
+        },
+        params);
+    return st == hipSuccess ? PS_OK : PS_ERR_HIP;
+}
 
 // Launchers.  Arguments have already been validated by the entry points in
 // api.hip; each returns PS_OK or PS_ERR_HIP.
@@ -28,18 +48,20 @@ int launch_conv_general(const void *x, const void *w, const float *conv_bias, co
                         int kH, int kW, int cs, int cp, int cd, int OH, int OW, float scale,
                         int pk, int ps, int pp, int pd, int PH, int PW, hipStream_t stream);
 
+// Transposed conv k4 s2 d1, any padding `pad` (OH, OW already include it and the
+// output_padding), Cout a multiple of 16 up to 256.
 int launch_convT_softmax(const float *x, const float *w, const float *convT_bias,
                          const float *bias2, float *y, int N, int Cin, int H, int W, int Cout,
-                         int OH, int OW, float scale, hipStream_t stream);
+                         int OH, int OW, int pad, float scale, hipStream_t stream);
 
 // bf16 x, w and y (uint16 bit patterns), fp32 accumulation; Cout a multiple of 32.
 int launch_convT_softmax_bf16(const uint16_t *x, const uint16_t *w, const float *convT_bias,
                               const float *bias2, uint16_t *y, int N, int Cin, int H, int W,
-                              int Cout, int OH, int OW, float scale, hipStream_t stream);
+                              int Cout, int OH, int OW, int pad, float scale, hipStream_t stream);
 
 // The same transposed conv without the softmax epilogue (y = convT + bias).
 int launch_convT(const float *x, const float *w, const float *convT_bias, float *y, int N,
-                 int Cin, int H, int W, int Cout, int OH, int OW, hipStream_t stream);
+                 int Cin, int H, int W, int Cout, int OH, int OW, int pad, hipStream_t stream);
 
 // Post-processing stages of the unfused pipelines.
 int launch_tanh_scale_bias_maxpool(const void *y, const float *bias2, void *out, int dtype, int N,

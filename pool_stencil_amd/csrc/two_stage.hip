@@ -133,14 +133,11 @@ int launch_tanh_scale_bias_maxpool(const void *y, const float *bias2, void *out,
     }
     const dim3 grid((unsigned)((OH * OW + 255) / 256), (unsigned)(planes < 65535 ? planes : 65535));
     if (dtype == PS_BF16)
-        hipLaunchKernelGGL(tanh_scale_bias_maxpool_k<uint16_t>, grid, dim3(256), 0, stream,
-                           (const uint16_t *)y, bias2, (uint16_t *)out, C, H, W, OH, OW, k, s, p,
-                           d, scale, (int)planes);
-    else
-        hipLaunchKernelGGL(tanh_scale_bias_maxpool_k<float>, grid, dim3(256), 0, stream,
-                           (const float *)y, bias2, (float *)out, C, H, W, OH, OW, k, s, p, d,
-                           scale, (int)planes);
-    return hipGetLastError() == hipSuccess ? PS_OK : PS_ERR_HIP;
+        return launch(tanh_scale_bias_maxpool_k<uint16_t>, grid, dim3(256), 0, stream,
+                      (const uint16_t *)y, bias2, (uint16_t *)out, C, H, W, OH, OW, k, s, p, d,
+                      scale, (int)planes);
+    return launch(tanh_scale_bias_maxpool_k<float>, grid, dim3(256), 0, stream, (const float *)y,
+                  bias2, (float *)out, C, H, W, OH, OW, k, s, p, d, scale, (int)planes);
 }
 
 int launch_softmax_bias_scale_sigmoid(const float *y, const float *bias2, float *out, int N,
@@ -149,18 +146,16 @@ int launch_softmax_bias_scale_sigmoid(const float *y, const float *bias2, float 
     if (hw > 0x7fffffff - 256) return PS_ERR_UNSUPPORTED;
     const dim3 grid((unsigned)((hw + 255) / 256), (unsigned)(N < 65535 ? N : 65535));
     if (C <= 32)
-        hipLaunchKernelGGL(softmax_bias_scale_sigmoid_k<32>, grid, dim3(256), 0, stream, y, bias2,
-                           out, N, C, (int)hw, scale);
-    else if (C <= 64)
-        hipLaunchKernelGGL(softmax_bias_scale_sigmoid_k<64>, grid, dim3(256), 0, stream, y, bias2,
-                           out, N, C, (int)hw, scale);
-    else if (C <= 128)
-        hipLaunchKernelGGL(softmax_bias_scale_sigmoid_k<128>, grid, dim3(256), 0, stream, y,
-                           bias2, out, N, C, (int)hw, scale);
-    else
-        hipLaunchKernelGGL(softmax_bias_scale_sigmoid_k<0>, grid, dim3(256), 0, stream, y, bias2,
-                           out, N, C, (int)hw, scale);
-    return hipGetLastError() == hipSuccess ? PS_OK : PS_ERR_HIP;
+        return launch(softmax_bias_scale_sigmoid_k<32>, grid, dim3(256), 0, stream, y, bias2, out,
+                      N, C, (int)hw, scale);
+    if (C <= 64)
+        return launch(softmax_bias_scale_sigmoid_k<64>, grid, dim3(256), 0, stream, y, bias2, out,
+                      N, C, (int)hw, scale);
+    if (C <= 128)
+        return launch(softmax_bias_scale_sigmoid_k<128>, grid, dim3(256), 0, stream, y, bias2,
+                      out, N, C, (int)hw, scale);
+    return launch(softmax_bias_scale_sigmoid_k<0>, grid, dim3(256), 0, stream, y, bias2, out, N,
+                  C, (int)hw, scale);
 }
 
 }  // namespace ps

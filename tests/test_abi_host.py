@@ -183,8 +183,11 @@ def test_convT_validation(ps):
     assert _convT(lib, k=3) == ps.PS_ERR_UNSUPPORTED
     assert _convT(lib, s=3) == ps.PS_ERR_UNSUPPORTED
     assert _convT(lib, Cout=24) == ps.PS_ERR_UNSUPPORTED
-    assert _convT(lib, Cout=144) == ps.PS_ERR_UNSUPPORTED
+    assert _convT(lib, Cout=272) == ps.PS_ERR_UNSUPPORTED
     assert _convT(lib, Cin=80) == ps.PS_ERR_UNSUPPORTED     # a class's weights exceed the LDS
+    assert _convT(lib, Cout=160) == ps.PS_ERR_UNSUPPORTED   # likewise at Cin = 64
+    assert _convT(lib, Cout=256, Cin=40) == ps.PS_ERR_UNSUPPORTED
+    assert _convT(lib, p=5, H=2, W=2, op=0) == ps.PS_ERR_SHAPE   # (2-1)*2 - 10 + 4 < 1
     assert _convT(lib, Cin=76, Cout=128, N=1 << 12, H=64, W=64) == ps.PS_ERR_UNSUPPORTED  # >= 2^29
     assert _convT(lib, x=MISALIGNED) == ps.PS_ERR_ALIGN
 

@@ -285,6 +285,18 @@ CONVT_CASES = [
     dict(N=1, Cin=32, H=12, W=20, Cout=112),
     dict(N=1, Cin=70, H=6, W=70, Cout=128),       # Cin not a multiple of 4, 150 KB of weights
     dict(N=4, Cin=7, H=13, W=9, Cout=64, output_padding=0),  # channels past Cin, last image
+    # any padding: the class -> kernel tap / input offset mapping moves with its parity
+    dict(N=2, Cin=16, H=9, W=11, Cout=64, pad=0),
+    dict(N=1, Cin=16, H=10, W=7, Cout=32, pad=0, output_padding=0),
+    dict(N=2, Cin=20, H=9, W=12, Cout=48, pad=2),
+    dict(N=1, Cin=64, H=8, W=9, Cout=128, pad=3, output_padding=0),
+    dict(N=1, Cin=8, H=12, W=10, Cout=16, pad=5),
+    dict(N=1, Cin=4, H=3, W=3, Cout=16, pad=3),               # 1x1 .. output rows
+    # more than 128 channels: one 16-pixel group per wave tile
+    dict(N=2, Cin=64, H=7, W=9, Cout=144),
+    dict(N=1, Cin=36, H=6, W=10, Cout=256),                   # the largest weight tile
+    dict(N=1, Cin=20, H=5, W=7, Cout=240, pad=2, scale=-0.7),
+    dict(N=3, Cin=9, H=4, W=6, Cout=176, pad=0, convT_bias=False),
 ]
 
 
@@ -316,6 +328,15 @@ CONVT_BF16_CASES = [
     dict(N=2, Cin=64, H=4, W=64, Cout=128, scale=-0.5),
     dict(N=1, Cin=32, H=3, W=160, Cout=64),       # rows longer than a work item
     dict(N=1, Cin=16, H=2, W=256, Cout=32, output_padding=0),
+    # any padding, both kernels (W % 8 == 0 takes the staged one)
+    dict(N=2, Cin=16, H=9, W=16, Cout=64, pad=0),             # positions up to column W + 1
+    dict(N=1, Cin=16, H=7, W=8, Cout=32, pad=0, output_padding=0),
+    dict(N=2, Cin=24, H=6, W=24, Cout=96, pad=2),
+    dict(N=1, Cin=64, H=5, W=16, Cout=128, pad=3, output_padding=0),
+    dict(N=1, Cin=8, H=12, W=40, Cout=32, pad=5),
+    dict(N=2, Cin=16, H=9, W=11, Cout=64, pad=0),             # the pixel-tile kernel
+    dict(N=1, Cin=20, H=7, W=13, Cout=96, pad=2),
+    dict(N=1, Cin=13, H=6, W=9, Cout=32, pad=3, output_padding=0),
 ]
 
 

@@ -55,6 +55,9 @@ CONVT2D_CASES = [
     dict(N=1, Cin=13, H=5, W=11, Cout=48, output_padding=0),
     dict(N=1, Cin=1, H=1, W=1, Cout=16),
     dict(N=2, Cin=32, H=8, W=8, Cout=112, convT_bias=False),
+    dict(N=1, Cin=16, H=6, W=9, Cout=64, pad=0),
+    dict(N=1, Cin=12, H=7, W=6, Cout=48, pad=3, output_padding=0),
+    dict(N=1, Cin=32, H=5, W=6, Cout=256),
 ]
 
 
