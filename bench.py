@@ -23,13 +23,20 @@ synthetic workload, on inputs already resident in HBM:
   conv_general x fp32 [32,64,128,128] -> conv 64->128 k3 p1 + tanh + *2 + bias
               + maxpool k3 s2 p1 (overlapping windows) -> [32,128,64,64]
               (77.31 GFLOP: every 128x128 conv output is read by some window)
+  tiny_conv   x fp32 [2,8,32,32] -> conv 8->16 k3 + tanh + *2 + bias + maxpool 4
+              -> [2,16,7,7] (3.61 MFLOP: a launch-latency-bound call, reported in us)
 
 `value` is the fused conv+maxpool throughput (GFLOP/s, fp32) -- the first
 figure of the headline metric; the max-pool's GB/s (the second figure) and the
 other two operations are reported in `ops` of the same line, each with its
 roofline fraction.  Per-kernel times come from HIP events recorded on the
 stream the kernels run on (torch's current stream), averaged over the timed
-steps.  Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
+steps.  Each operation also carries `cpu_baseline`: the CPU oracle (plain C,
+double precision, OpenMP) timed on the host cores on a bounded slice of the
+same workload, with the host's CPU model and thread counts.  The line also
+records the GPU clocks rocm-smi reports while the fused conv runs and the
+bandwidth of a plain device copy (a practical HBM ceiling next to 8 TB/s).
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
 from __future__ import annotations
 
@@ -57,6 +64,7 @@ CONVT_INTER_BYTES = 128 * 128 * 129 * 129 * 4      # the stored convT output
 CONVT_FLOP = 2 * 128 * 64 * 128 * 255 * 255
 CONVT_BYTES = 128 * 64 * 64 * 64 * 4 + 128 * 128 * 129 * 129 * 4 + 64 * 128 * 16 * 4
 CONVT_BF16_BYTES = 128 * 64 * 64 * 64 * 2 + 128 * 128 * 129 * 129 * 2 + 64 * 128 * 16 * 2
+TINY_FLOP = 2 * 72 * 2 * 16 * 28 * 28              # the 28x28 conv outputs the pool reads
 
 # HBM bytes per launch, from two rocprofv3 --pmc passes over this script (FETCH_SIZE,
 # then WRITE_SIZE, KiB per dispatch), each scaled by what the same counter reads for a
@@ -112,7 +120,7 @@ def parse():
                     help="skip the oracle timing (profiling runs)")
     ap.add_argument("--ops",
                     default="conv,maxpool,convT,conv_bf16,conv_general,convT_bf16,maxpool_s2,"
-                            "maxpool_d2,conv_2stage,convT_2stage")
+                            "maxpool_d2,conv_2stage,convT_2stage,tiny_conv")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a 2 GiB device-to-device copy instead (counter calibration)")
     return ap.parse_args()
@@ -220,6 +228,13 @@ def main():
         outtb = torch.empty((128, 128, 129, 129), dtype=torch.bfloat16, device=dev)
         runs["convT_bf16"] = lambda xtb=xtb, wtb=wtb, cbtb=cbtb, b2tb=b2tb, outtb=outtb: (
             ps.convT_softmax_bias_scale_sigmoid(xtb, wtb, cbtb, b2tb, 2.0, 2, 1, 1, 1, out=outtb))
+        del c
+    if "tiny_conv" in ops:
+        c = inputgen.workload("tiny_conv")
+        xs, ws, cbs, b2s = put(c["x"]), put(c["w"]), put(c["conv_bias"]), put(c["bias2"])
+        outs = torch.empty((2, 16, 7, 7), dtype=torch.float32, device=dev)
+        runs["tiny_conv"] = lambda xs=xs, ws=ws, cbs=cbs, b2s=b2s, outs=outs: (
+            ps.conv_tanh_scale_bias_maxpool(xs, ws, cbs, b2s, 2.0, 4, out=outs))
         del c
     stages = {}   # op -> list of stage callables (timed one by one)
     if "conv_2stage" in ops:
@@ -374,10 +389,32 @@ def main():
             "stage2_roofline": {"bound": "hbm", "achieved": b1 / 1e9, "peak": PEAK_HBM / 1e9,
                                 "unit": "GB/s", "frac": b1 / PEAK_HBM}}
 
+    if "tiny_conv" in runs:
+        mean, med, mn = stats("tiny_conv")
+        out_ops["tiny_conv"] = {
+            "value": mean * 1e3, "unit": "us", "ms_mean": mean, "ms_median": med, "ms_min": mn,
+            "gflops": TINY_FLOP / (mean * 1e-3) / 1e9,
+            "roofline": None, "note": "launch-latency bound (3.61 MFLOP): no roofline claim"}
+
+    # GPU clocks while the fused conv runs, and a plain device copy as a practical HBM
+    # ceiling (outside the timed step)
+    clocks = sample_clocks(runs.get("conv"))
+    gpu_info = {"clocks_during_conv": clocks, "hbm_copy": copy_ceiling()}
+    sclk = mhz(clocks, "sclk clock speed")
+    if sclk:
+        # the published 157.3 TFLOP/s is 256 CUs x 2.4 GHz x 256 fp32 FLOP per clock per CU
+        ncu = torch.cuda.get_device_properties(dev).multi_processor_count
+        gpu_info["fp32_peak_at_observed_sclk_TFLOPs"] = ncu * sclk * 1e6 * 256 / 1e12
     head = "conv" if "conv" in out_ops else next(iter(out_ops))
     cpu = None
-    if not args.no_cpu_baseline and head == "conv":
-        cpu = cpu_baseline()
+    host = host_info()
+    if not args.no_cpu_baseline:
+        for op in CPU_SAMPLES:
+            if op in out_ops:
+                out_ops[op]["cpu_baseline"] = cpu_baseline(op, host)
+                print(f"[bench] cpu baseline {op}: {out_ops[op]['cpu_baseline']['seconds']:.2f}s",
+                      file=sys.stderr, flush=True)
+        cpu = out_ops[head].get("cpu_baseline")
 
     line = {
         "metric": "fused conv+maxpool GFLOP/s & maxpool GB/s, % of MI355X roofline, 1 GPU",
@@ -411,28 +448,131 @@ def main():
         "roofline": out_ops[head]["roofline"],
         "cpu_baseline": cpu,
         "maxpool_GBps": out_ops.get("maxpool", {}).get("value"),
+        "host": host,
+        "gpu": gpu_info,
         "ops": out_ops,
     }
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline():
-    """The oracle (plain C, fp64, OpenMP) on a bounded slice of the conv workload."""
+def host_info():
+    """CPU model, the cores this process may run on, and the oracle's OpenMP threads."""
+    import oracle
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "affinity_cores": len(os.sched_getaffinity(0)),
+            "omp_threads": oracle.num_threads()}
+
+
+def sample_clocks(fn, seconds=1.5):
+    """rocm-smi's current clocks, read while `fn` (the fused conv) runs back to back."""
+    import subprocess
+    import torch
+    if fn is None:
+        return None
+    try:
+        proc = subprocess.Popen(["rocm-smi", "--showclocks", "--json"], stdout=subprocess.PIPE,
+                                stderr=subprocess.DEVNULL, text=True)
+    except OSError as e:
+        return {"error": str(e)}
+    t0 = time.perf_counter()
+    while proc.poll() is None and time.perf_counter() - t0 < seconds + 20:
+        for _ in range(200):
+            fn()
+        torch.cuda.synchronize()
+    try:
+        out, _ = proc.communicate(timeout=20)
+        data = json.loads(out)
+    except Exception as e:  # noqa: BLE001 - report, do not fail the bench
+        proc.kill()
+        return {"error": repr(e)}
+    card = next(iter(data.values())) if isinstance(data, dict) and data else {}
+    return {k.rstrip(":"): v for k, v in card.items() if "clock" in k.lower()}
+
+
+def mhz(clocks, key):
+    """The MHz figure of a rocm-smi clock entry such as '(2342Mhz)', or None."""
+    import re
+    if not isinstance(clocks, dict) or key not in clocks:
+        return None
+    m = re.search(r"([0-9.]+)\s*mhz", str(clocks[key]), re.I)
+    return float(m.group(1)) if m else None
+
+
+def copy_ceiling(steps=10):
+    """A device-to-device copy of 1 GiB (read + write), the practical ceiling of a
+    mixed read/write stream on this GPU."""
+    import torch
+    n = 1 << 28
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(steps):
+        y.copy_(x)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    del x, y
+    torch.cuda.empty_cache()
+    return {"bytes_per_copy": 2 * 4 * n, "ms": ms, "GBps": 2 * 4 * n / (ms * 1e-3) / 1e9,
+            "what": "torch device copy of 1 GiB (1 GiB read + 1 GiB written)"}
+
+
+# op -> (workload, images in the sample, algorithmic work of the sample, unit)
+CPU_SAMPLES = {
+    "conv": ("conv", 128, CONV_FLOP, "GFLOP/s"),
+    "conv_bf16": ("conv_bf16", 128, CONV_FLOP, "GFLOP/s"),
+    "maxpool": ("maxpool", 32, POOL_BYTES, "GB/s"),
+    "maxpool_s2": ("maxpool", 32, POOL_S2_BYTES, "GB/s"),
+    "maxpool_d2": ("maxpool", 32, POOL_D2_BYTES, "GB/s"),
+    "convT": ("convT", 32, CONVT_FLOP / 4, "GFLOP/s"),
+    "convT_bf16": ("convT_bf16", 32, CONVT_FLOP / 4, "GFLOP/s"),
+    "conv_general": ("conv_general", 8, CONV_GENERAL_FLOP / 4, "GFLOP/s"),
+    "tiny_conv": ("tiny_conv", 2, TINY_FLOP, "us"),
+}
+POOL_ARGS = {"maxpool": (4, 1, 1, 1), "maxpool_s2": (3, 2, 1, 1), "maxpool_d2": (3, 1, 2, 2)}
+
+
+def cpu_baseline(op, host):
+    """The oracle (plain C, fp64, OpenMP) on a bounded slice of the op's workload, in
+    the op's unit, counted with the same algorithmic work as the GPU figure."""
     import oracle
     import inputgen
-    c = inputgen.workload("conv")
-    n_img = int(os.environ.get("PS_CPU_IMAGES", "128"))
-    c1 = dict(c)
-    c1["x"] = c["x"][:n_img]
-    c1["N"] = n_img
-    t = time.perf_counter()
-    oracle.conv_tanh_scale_bias_maxpool(c1)
-    dt = time.perf_counter() - t
-    flop = CONV_FLOP / 128 * n_img
-    return {"value": flop / dt / 1e9, "unit": "GFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle", "seconds": dt,
-            "sample": f"first {n_img} of 128 images of the conv workload (full fused op in "
-                      f"written order, double precision); GFLOP counted as for the GPU"}
+    name, n_img, work, unit = CPU_SAMPLES[op]
+    c = inputgen.workload(name)
+    total = c["N"]
+    if op in POOL_ARGS:
+        x = c["x"][:n_img]
+        t = time.perf_counter()
+        oracle.maxpool2d(x, *POOL_ARGS[op])
+        dt = time.perf_counter() - t
+        what = f"max-pool of the first {n_img} of {total} images, float32 (exact)"
+    else:
+        c1 = dict(c, x=c["x"][:n_img], N=n_img)
+        fn = (oracle.convT_softmax_bias_scale_sigmoid if name.startswith("convT")
+              else oracle.conv_tanh_scale_bias_maxpool)
+        reps = 200 if op == "tiny_conv" else 1
+        t = time.perf_counter()
+        for _ in range(reps):
+            fn(c1)
+        dt = (time.perf_counter() - t) / reps
+        what = (f"the first {n_img} of {total} images of the {name} workload, the full fused "
+                f"op in written order, double precision")
+    value = dt * 1e6 if unit == "us" else work / dt / 1e9   # GB/s or GFLOP/s
+    return {"value": value, "unit": unit, "cores": host["omp_threads"], "kind": "oracle",
+            "seconds": dt, "sample": what + "; work counted as for the GPU figure",
+            "cpu_model": host["cpu_model"], "affinity_cores": host["affinity_cores"]}
 
 
 if __name__ == "__main__":
