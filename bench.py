@@ -72,14 +72,14 @@ TINY_FLOP = 2 * 72 * 2 * 16 * 28 * 28              # the 28x28 conv outputs the 
 # x1.0.  `src` is the hash of the kernel's sources when the counters were taken; a
 # kernel edited since then reports traffic null.  See profiles/traffic_*.md.
 TRAFFIC = {
-    "conv": {"src": "56935f836ef1ce8d", "fetch_bytes": 266687112, "write_bytes": 130625824},
-    "conv_bf16": {"src": "56935f836ef1ce8d", "fetch_bytes": 136709847, "write_bytes": 79985968},
-    "maxpool": {"src": "ae3c7bf4d49a6384", "fetch_bytes": 2160264933, "write_bytes": 2140766640},
-    "maxpool_s2": {"src": "ae3c7bf4d49a6384", "fetch_bytes": 2176859472, "write_bytes": 536870912},
-    "maxpool_d2": {"src": "ae3c7bf4d49a6384", "fetch_bytes": 2266622156, "write_bytes": 2147483648},
-    "convT": {"src": "f6e144b9d0e20781", "fetch_bytes": 596515363, "write_bytes": 2346226880},
-    "convT_bf16": {"src": "4dd80d9c4526d1a3", "fetch_bytes": 119830774, "write_bytes": 589941136},
-    "conv_general": {"src": "683da3031f3318fe", "fetch_bytes": 136919185, "write_bytes": 69272144},
+    "conv": {"src": "641af60c69dd6ee4", "fetch_bytes": 266686969, "write_bytes": 130622224},
+    "conv_bf16": {"src": "641af60c69dd6ee4", "fetch_bytes": 136709774, "write_bytes": 80035856},
+    "maxpool": {"src": "f9f4a82d532a67be", "fetch_bytes": 2160264222, "write_bytes": 2140716768},
+    "maxpool_s2": {"src": "f9f4a82d532a67be", "fetch_bytes": 2176869184, "write_bytes": 536870912},
+    "maxpool_d2": {"src": "f9f4a82d532a67be", "fetch_bytes": 2266858564, "write_bytes": 2147483648},
+    "convT": {"src": "333c26b93de1daf3", "fetch_bytes": 604640218, "write_bytes": 2347717312},
+    "convT_bf16": {"src": "68ece0f4911cfb2c", "fetch_bytes": 119831797, "write_bytes": 590689392},
+    "conv_general": {"src": "a6c2d8a9bfe78480", "fetch_bytes": 136918791, "write_bytes": 69311232},
 }
 KERNEL_SOURCES = {
     "conv": ["conv_pool.hip", "ps_internal.h"],
@@ -117,7 +117,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true",
-                    help="skip the oracle timing (profiling runs)")
+                    help="skip the oracle timing and the clock probe (profiling runs)")
     ap.add_argument("--ops",
                     default="conv,maxpool,convT,conv_bf16,conv_general,convT_bf16,maxpool_s2,"
                             "maxpool_d2,conv_2stage,convT_2stage,tiny_conv")
@@ -158,6 +158,10 @@ def main():
     if args.copy_calibration:
         copy_calibration(args.steps)
         return
+
+    # the clock probe's helper starts before anything here touches the GPU (profiling
+    # runs skip it)
+    helper = None if args.no_cpu_baseline else start_clock_helper()
 
     import numpy as np
     import torch
@@ -398,7 +402,7 @@ def main():
 
     # GPU clocks while the fused conv runs, and a plain device copy as a practical HBM
     # ceiling (outside the timed step)
-    clocks = sample_clocks(runs.get("conv"))
+    clocks = sample_clocks(helper, runs.get("conv"))
     gpu_info = {"clocks_during_conv": clocks, "hbm_copy": copy_ceiling()}
     sclk = mhz(clocks, "sclk clock speed")
     if sclk:
@@ -471,29 +475,56 @@ def host_info():
             "omp_threads": oracle.num_threads()}
 
 
-def sample_clocks(fn, seconds=1.5):
-    """rocm-smi's current clocks, read while `fn` (the fused conv) runs back to back."""
-    import subprocess
-    import torch
-    if fn is None:
-        return None
+CLOCK_HELPER = r"""
+import subprocess, sys
+for _ in sys.stdin:
     try:
-        proc = subprocess.Popen(["rocm-smi", "--showclocks", "--json"], stdout=subprocess.PIPE,
-                                stderr=subprocess.DEVNULL, text=True)
-    except OSError as e:
-        return {"error": str(e)}
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True,
+                           text=True, timeout=30)
+        out = r.stdout
+    except Exception as e:
+        out = ""
+    sys.stdout.write(out.replace(chr(10), " ") + chr(10))
+    sys.stdout.flush()
+"""
+
+
+def start_clock_helper():
+    """A helper process that runs rocm-smi on request.  It is started before this
+    process touches the GPU, so neither it nor the rocm-smi it starts inherits an
+    initialised GPU runtime."""
+    import subprocess
+    try:
+        return subprocess.Popen([sys.executable, "-c", CLOCK_HELPER], stdin=subprocess.PIPE,
+                                stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True)
+    except OSError:
+        return None
+
+
+def sample_clocks(helper, fn, seconds=20.0):
+    """rocm-smi's current clocks, read while `fn` (the fused conv) runs back to back."""
+    import threading
+    import torch
+    if helper is None or fn is None:
+        return None
+    reply = []
+    helper.stdin.write("go\n")
+    helper.stdin.flush()
+    reader = threading.Thread(target=lambda: reply.append(helper.stdout.readline()), daemon=True)
+    reader.start()
     t0 = time.perf_counter()
-    while proc.poll() is None and time.perf_counter() - t0 < seconds + 20:
+    while reader.is_alive() and time.perf_counter() - t0 < seconds:
         for _ in range(200):
             fn()
         torch.cuda.synchronize()
+    helper.stdin.close()
     try:
-        out, _ = proc.communicate(timeout=20)
-        data = json.loads(out)
-    except Exception as e:  # noqa: BLE001 - report, do not fail the bench
-        proc.kill()
-        return {"error": repr(e)}
-    card = next(iter(data.values())) if isinstance(data, dict) and data else {}
+        data = json.loads(reply[0]) if reply else None
+    except ValueError:
+        data = None
+    if not isinstance(data, dict) or not data:
+        return None
+    card = next(iter(data.values()))
     return {k.rstrip(":"): v for k, v in card.items() if "clock" in k.lower()}
 
 
