@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpool_stencil.so")
 SOURCES = ["api.hip", "maxpool.hip", "conv_pool.hip", "conv_general.hip", "convt_softmax.hip",
-           "convt_softmax_bf16.hip", "two_stage.hip"]
+           "convt_rows.hip", "convt_softmax_bf16.hip", "two_stage.hip"]
 ARCH = os.environ.get("PS_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

@@ -402,15 +402,23 @@ int launch_cout(const float *x, const float *w, const float *cb, const float *b2
 
 }  // namespace
 
+// The row-class kernel (convt_rows.hip: whole output lines per workgroup) where its
+// envelope allows; the class-per-workgroup kernel above otherwise.
 int launch_convT_softmax(const float *x, const float *w, const float *convT_bias,
                          const float *bias2, float *y, int N, int Cin, int H, int W, int Cout,
                          int OH, int OW, int pad, float scale, hipStream_t stream) {
+    const int st = launch_convT_rows(x, w, convT_bias, bias2, y, N, Cin, H, W, Cout, OH, OW, pad,
+                                     scale, true, stream);
+    if (st != PS_ERR_UNSUPPORTED) return st;
     return launch_cout<true>(x, w, convT_bias, bias2, y, N, Cin, H, W, Cout, OH, OW, pad, scale,
                              stream);
 }
 
 int launch_convT(const float *x, const float *w, const float *convT_bias, float *y, int N,
                  int Cin, int H, int W, int Cout, int OH, int OW, int pad, hipStream_t stream) {
+    const int st = launch_convT_rows(x, w, convT_bias, nullptr, y, N, Cin, H, W, Cout, OH, OW,
+                                     pad, 1.f, false, stream);
+    if (st != PS_ERR_UNSUPPORTED) return st;
     return launch_cout<false>(x, w, convT_bias, nullptr, y, N, Cin, H, W, Cout, OH, OW, pad, 1.f,
                               stream);
 }

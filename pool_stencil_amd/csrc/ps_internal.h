@@ -54,6 +54,13 @@ int launch_convT_softmax(const float *x, const float *w, const float *convT_bias
                          const float *bias2, float *y, int N, int Cin, int H, int W, int Cout,
                          int OH, int OW, int pad, float scale, hipStream_t stream);
 
+// The row-class transposed conv (softmax epilogue or plain + bias): Cout = 128,
+// Cin <= 64, W a multiple of 4, at least 64 column positions per output row.
+// PS_ERR_UNSUPPORTED (before any HIP call) outside that envelope.
+int launch_convT_rows(const float *x, const float *w, const float *cb, const float *b2, float *y,
+                      int N, int Cin, int H, int W, int Cout, int OH, int OW, int pad,
+                      float scale, bool softmax, hipStream_t stream);
+
 // bf16 x, w and y (uint16 bit patterns), fp32 accumulation; Cout a multiple of 32.
 int launch_convT_softmax_bf16(const uint16_t *x, const uint16_t *w, const float *convT_bias,
                               const float *bias2, uint16_t *y, int N, int Cin, int H, int W,

@@ -300,6 +300,23 @@ CONVT_CASES = [
 ]
 
 
+# the row-class kernel: Cout 128, Cin <= 64, W a multiple of 4, >= 64 column
+# positions per output row (segments of a plane per workgroup when there are fewer
+# planes than CUs, so several cases start mid-plane; N = 64 gives units of several
+# tiles, the steady-state row ring)
+CONVT_ROWS_CASES = [
+    dict(N=2, Cin=64, H=5, W=64, Cout=128),
+    dict(N=1, Cin=64, H=7, W=64, Cout=128, output_padding=0),
+    dict(N=3, Cin=20, H=4, W=68, Cout=128, pad=0),
+    dict(N=2, Cin=37, H=5, W=72, Cout=128, pad=2, scale=-0.6, convT_bias=False),
+    dict(N=1, Cin=64, H=6, W=76, Cout=128, pad=3, output_padding=0),
+    dict(N=1, Cin=16, H=9, W=84, Cout=128),
+    dict(N=1, Cin=8, H=6, W=68, Cout=128, pad=5),
+    dict(N=64, Cin=64, H=6, W=64, Cout=128),
+]
+CONVT_CASES += CONVT_ROWS_CASES
+
+
 @pytest.mark.parametrize("kw", CONVT_CASES)
 def test_convT_small(dev, kw):
     c = inputgen.random_convT_case(4000, **kw)
