@@ -58,6 +58,11 @@ struct TileGeom {
     static constexpr int COLS = PK * T + 2;  // input columns per tile (kW = 3)
     static constexpr int Q = T + 1;          // entries per column-residue plane
     static constexpr int RS = PK * Q;        // entries per tile row
+    // fp32 tile: one more entry per plane, so the (masked) columns of a row's last
+    // 16-byte group, up to column 4 * ceil(COLS / 4) - 1 <= PK*T + PK - 1 for PK >= 5
+    // and <= PK*T + 3 otherwise, land on unused entries of their own row
+    static constexpr int QF = T + 2;
+    static constexpr int RSF = PK * QF;
 };
 
 // ---------------------------------------------------------------- fp32 ---
@@ -89,10 +94,10 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? PS_CONV_MIN_WAVES : 1)) void c
     const float *__restrict__ b2, float *__restrict__ y, int Cin, int H, int W, int Cout,
     int pad, int PH, int PW, float scale, int npwt) {
     using G = TileGeom<PK, NPW>;
-    constexpr int PS = pad_words_16mod64(G::ROWS * G::RS);  // words per input channel
+    constexpr int PS = pad_words_16mod64(G::ROWS * G::RSF);  // words per input channel
     constexpr int CINP = 4 * CING;
-    // the halo tile, and a 64-word dummy area for the fill's values with no place
-    __shared__ float tile[CINP * PS + 64];
+    // the halo tile
+    __shared__ float tile[CINP * PS];
     __shared__ float s_bias[2][64];  // conv bias, bias2 of the current 64-channel tile
 
     const uint32_t L = xcd_remap(blockIdx.x, gridDim.x);
@@ -105,7 +110,11 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? PS_CONV_MIN_WAVES : 1)) void c
     const int j = lane & 15;  // pooled column within the 16-wide group (B/D column)
     const int g4 = lane >> 4; // lane group: input channel within a K-step; D row block
 
-    // A operands of channel tile ct: w[co = ct + 16*nt + j][ci = 4*g + g4][tap]
+    // A operands of channel tile ct: sgn * w[co = ct + 16*nt + j][ci = 4*g + g4][tap].
+    // sgn = -1 for scale < 0 makes the window max of the products the negated window
+    // minimum of the conv sums, so the pool loop is a plain max (no multiply per value).
+    const float sgn = scale < 0.f ? -1.f : 1.f;
+    const uint32_t sgn_bit = scale < 0.f ? 0x80000000u : 0u;
     float wr[4][9][CING];
     auto load_weights = [&](int ct) {
 #pragma unroll
@@ -118,8 +127,10 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? PS_CONV_MIN_WAVES : 1)) void c
                 const float *wp = w + ((size_t)(ok ? co : 0) * Cin + (ok ? ci : 0)) * 9;
 #pragma unroll
                 for (int tap = 0; tap < 9; ++tap) {
+                    // (the sign as a bit flip after the select: multiplying inside it
+                    // turned the unconditional loads into one branch and wait per load)
                     const float v = wp[tap];
-                    wr[nt][tap][g] = ok ? v : 0.f;
+                    wr[nt][tap][g] = __uint_as_float(__float_as_uint(ok ? v : 0.f) ^ sgn_bit);
                 }
             }
         }
@@ -136,79 +147,144 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? PS_CONV_MIN_WAVES : 1)) void c
     stage_bias(0);
 
     // ---- stage the zero-padded halo tile ----
-    // Every thread first issues all of its global loads (16-byte vectors when the
-    // tile's columns are 16-byte aligned), then writes them to LDS, so the loads
-    // of the whole tile are in flight together.
+    // Tile rows (input channel, input row) are streamed by whole waves: lane l of a wave
+    // loads the l-th 4-column group of the row, so the per-lane column offsets, their
+    // validity and the lane's LDS words are computed once and a row costs one load, one
+    // select and four LDS writes (per-vector index arithmetic had cost about 35 VALU
+    // instructions per 16-byte load, and on this chip VALU time adds to the matrix
+    // cores' time).  Groups past the last whole 64 of a row go through a short flat loop
+    // over all threads.  Every load is issued before any LDS write of its batch.
+    // Range-checked buffer loads over image n (below 2^31 bytes, host check): a value
+    // outside the image -- the conv's zero padding -- gets a masked offset and reads zero.
     const int ir0 = PK * ph - pad;
     const int ic0 = PK * pwt * G::T - pad;
     const float *xn = x + (size_t)n * Cin * H * W;
+    const int wvu = __builtin_amdgcn_readfirstlane(wv);  // (wave-uniform: rows in scalars)
+    constexpr uint32_t kMasked = 0x80000000u;
+    const __amdgpu_buffer_rsrc_t xr =
+        make_range_checked(xn, 4u * (uint32_t)Cin * (uint32_t)H * (uint32_t)W);
+    constexpr int NROWS = CINP * G::ROWS;     // tile rows
+    constexpr int NV = (G::COLS + 3) / 4;     // 4-column groups per tile row
+    constexpr int NFULL = NV / 64;            // groups covered by whole waves
+    constexpr int NTAIL = NV - 64 * NFULL;    // the rest of each row
+    constexpr int RPW = (NROWS + NPW - 1) / NPW;  // rows per wave
+    // image byte offset of tile row rr, and whether it lies in the image (and below Cin)
+    auto row_in = [&](int rr, uint32_t &off) {
+        const int ci = rr / G::ROWS, ir = ir0 + rr % G::ROWS;
+        off = 4u * ((uint32_t)(ci * H + ir) * (uint32_t)W);
+        return ci < Cin && ir >= 0 && ir < H;
+    };
+    auto row_lds = [&](int rr) { return (rr / G::ROWS) * PS + (rr % G::ROWS) * G::RSF; };
+    // LDS word of tile column c within its row (de-interleaved by c mod PK)
+    auto col_lds = [](int c) { return (c % PK) * G::QF + c / PK; };
     // (instantiated once per load width: a uniform test per element split the fill
     // into one branch per load)
     auto fill = [&](auto VEC) {
         constexpr bool vec = decltype(VEC)::value;
-        constexpr int NT = 64 * NPW;
-        constexpr int NV = (G::COLS + 3) / 4;           // 4-column groups per tile row
-        constexpr int TOTAL = CINP * G::ROWS * NV;
-        constexpr int PER = (TOTAL + NT - 1) / NT;
-        // Range-checked buffer loads over image n (below 2^31 bytes, host check): a value
-        // outside the image -- the conv's zero padding -- gets a masked offset and reads
-        // zero, so the loads are unconditional (bounds-checked loads compiled to a
-        // branch with about 50 instructions around each).  16-byte loads when the
-        // tile's columns are 16-byte aligned, else four 4-byte loads.
-        constexpr uint32_t kMasked = 0x80000000u;
-        const __amdgpu_buffer_rsrc_t xr =
-            make_range_checked(xn, 4u * (uint32_t)Cin * (uint32_t)H * (uint32_t)W);
-        // loads are issued FB vectors at a time (all of them when FB >= PER)
-        constexpr int FB = PS_CONV_FILL_BATCH > 0 && PS_CONV_FILL_BATCH < PER ? PS_CONV_FILL_BATCH : PER;
+        if constexpr (NFULL > 0) {
+            // per-lane column offsets (kMasked outside the image) and LDS words
+            uint32_t co[NFULL][vec ? 1 : 4];
+            int lw[NFULL][4];
 #pragma unroll
-        for (int i0 = 0; i0 < PER; i0 += FB) {
-            float4 buf[FB];
+            for (int ch = 0; ch < NFULL; ++ch) {
+                const int v = 64 * ch + lane;
+                const int ic = ic0 + 4 * v;
+                if constexpr (vec) {
+                    co[ch][0] = (ic >= 0) & (ic < W) ? 4u * (uint32_t)ic : kMasked;
+                } else {
 #pragma unroll
-            for (int ii = 0; ii < FB; ++ii) {
-                const int e = threadIdx.x + (i0 + ii) * NT;
-                const int u = e % NV;
-                const int row = e / NV;
-                const int r = row % G::ROWS;
-                const int ci = row / G::ROWS;
-                const int ir = ir0 + r, ic = ic0 + 4 * u;
-                // (bitwise: a short-circuit chain compiles to branches)
-                const bool rok = (i0 + ii < PER) & (e < TOTAL) & (ci < Cin) & (ir >= 0) & (ir < H);
-                const uint32_t o = 4u * ((uint32_t)(ci * H + ir) * (uint32_t)W + (uint32_t)ic);
+                    for (int k = 0; k < 4; ++k)
+                        co[ch][k] = (ic + k >= 0) & (ic + k < W) ? 4u * (uint32_t)(ic + k) : kMasked;
+                }
+#pragma unroll
+                for (int k = 0; k < 4; ++k) lw[ch][k] = col_lds(4 * v + k);
+            }
+            constexpr int FB = PS_CONV_FILL_BATCH > 0 && PS_CONV_FILL_BATCH < RPW ? PS_CONV_FILL_BATCH : RPW;
+#pragma unroll
+            for (int i0 = 0; i0 < RPW; i0 += FB) {
+                float4 buf[FB][NFULL];
+                // (no branch around the loads: a row past the last one reads zeros through
+                // masked offsets; branches here made the compiler wait before each load)
+#pragma unroll
+                for (int ii = 0; ii < FB; ++ii) {
+                    if (i0 + ii >= RPW) continue;  // compile-time after unrolling
+                    const int rr = wvu + NPW * (i0 + ii);
+                    uint32_t ro;
+                    const bool rok = (rr < NROWS) & row_in(rr < NROWS ? rr : 0, ro);
+#pragma unroll
+                    for (int ch = 0; ch < NFULL; ++ch) {
+                        if constexpr (vec) {
+                            const uint4 q = __builtin_bit_cast(
+                                uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           xr, rok ? co[ch][0] : kMasked, rok ? ro : 0u, 0));
+                            buf[ii][ch] = make_float4(__uint_as_float(q.x), __uint_as_float(q.y),
+                                                      __uint_as_float(q.z), __uint_as_float(q.w));
+                        } else {
+                            float vv[4];
+#pragma unroll
+                            for (int k = 0; k < 4; ++k)
+                                vv[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                                    xr, rok ? co[ch][k] : kMasked, rok ? ro : 0u, 0));
+                            buf[ii][ch] = make_float4(vv[0], vv[1], vv[2], vv[3]);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int ii = 0; ii < FB; ++ii) {
+                    const int rr = wvu + NPW * (i0 + ii);
+                    if (i0 + ii < RPW && rr < NROWS) {
+                        float *trow = tile + row_lds(rr);
+#pragma unroll
+                        for (int ch = 0; ch < NFULL; ++ch) {
+                            trow[lw[ch][0]] = buf[ii][ch].x;
+                            trow[lw[ch][1]] = buf[ii][ch].y;
+                            trow[lw[ch][2]] = buf[ii][ch].z;
+                            trow[lw[ch][3]] = buf[ii][ch].w;
+                        }
+                    }
+                }
+            }
+        }
+        if constexpr (NTAIL > 0) {
+            // the last NTAIL groups of every row: item e = (row, group) over all threads
+            constexpr int NT = 64 * NPW;
+            constexpr int TOTAL = NROWS * NTAIL;
+            constexpr int PER = (TOTAL + NT - 1) / NT;
+            float4 buf[PER];
+#pragma unroll
+            for (int i = 0; i < PER; ++i) {
+                const int e = threadIdx.x + i * NT;
+                const int rr = e / NTAIL, v = 64 * NFULL + e % NTAIL;
+                const int ic = ic0 + 4 * v;
+                uint32_t ro;
+                const bool rok = (e < TOTAL) & row_in(rr, ro);
                 if constexpr (vec) {
                     const bool ok = rok & (ic >= 0) & (ic < W);
                     const uint4 q = __builtin_bit_cast(
-                        uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, ok ? o : kMasked, 0, 0));
-                    buf[ii] = make_float4(__uint_as_float(q.x), __uint_as_float(q.y),
-                                          __uint_as_float(q.z), __uint_as_float(q.w));
+                        uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, ok ? ro + 4u * ic : kMasked, 0, 0));
+                    buf[i] = make_float4(__uint_as_float(q.x), __uint_as_float(q.y),
+                                         __uint_as_float(q.z), __uint_as_float(q.w));
                 } else {
                     float vv[4];
 #pragma unroll
                     for (int k = 0; k < 4; ++k) {
                         const bool ok = rok & (ic + k >= 0) & (ic + k < W);
                         vv[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-                            xr, ok ? o + 4u * k : kMasked, 0, 0));
+                            xr, ok ? ro + 4u * (ic + k) : kMasked, 0, 0));
                     }
-                    buf[ii] = make_float4(vv[0], vv[1], vv[2], vv[3]);
+                    buf[i] = make_float4(vv[0], vv[1], vv[2], vv[3]);
                 }
             }
-            // LDS writes: a value past the tile's columns or past the last vector goes
-            // to the dummy area instead (no branches)
 #pragma unroll
-            for (int ii = 0; ii < FB; ++ii) {
-                const int e = threadIdx.x + (i0 + ii) * NT;
-                if (i0 + ii < PER) {  // compile-time after unrolling
-                    const int u = e % NV;
-                    const int row = e / NV;
-                    const int r = row % G::ROWS;
-                    const int ci = row / G::ROWS;
-                    const int tbase = ci * PS + r * G::RS;
-                    const float vv[4] = {buf[ii].x, buf[ii].y, buf[ii].z, buf[ii].w};
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        const int c = 4 * u + k;
-                        const bool ok = (e < TOTAL) & (c < G::COLS);
-                        tile[ok ? tbase + (c % PK) * G::Q + c / PK : CINP * PS + (threadIdx.x & 63)] = vv[k];
-                    }
+            for (int i = 0; i < PER; ++i) {
+                const int e = threadIdx.x + i * NT;
+                if (e < TOTAL) {
+                    const int rr = e / NTAIL, v = 64 * NFULL + e % NTAIL;
+                    float *trow = tile + row_lds(rr);
+                    trow[col_lds(4 * v)] = buf[i].x;
+                    trow[col_lds(4 * v + 1)] = buf[i].y;
+                    trow[col_lds(4 * v + 2)] = buf[i].z;
+                    trow[col_lds(4 * v + 3)] = buf[i].w;
                 }
             }
         }
@@ -221,7 +297,6 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? PS_CONV_MIN_WAVES : 1)) void c
 
     const int pw = pwt * G::T + 16 * wv + j;
     const float *tb = tile + g4 * PS + 16 * wv + j;
-    const float sgn = scale < 0.f ? -1.f : 1.f;
     const uint32_t cplane = (uint32_t)(PH * PW);
     const __amdgpu_buffer_rsrc_t yr =
         make_range_checked(y + (size_t)n * Cout * cplane, 4u * (uint32_t)Cout * cplane);
@@ -241,7 +316,7 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? PS_CONV_MIN_WAVES : 1)) void c
 
 #pragma unroll 1
         for (int dy = 0; dy < PK; ++dy) {
-            const float *tr = tb + dy * G::RS;
+            const float *tr = tb + dy * G::RSF;
             // window columns in groups of DXG: fewer live accumulators when DXG < PK
             constexpr int DXG = PS_CONV_DXG > 0 && PS_CONV_DXG < PK ? PS_CONV_DXG : PK;
 #pragma unroll 1
@@ -260,7 +335,7 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? PS_CONV_MIN_WAVES : 1)) void c
 #pragma unroll
                         for (int kw = 0; kw < 3; ++kw) {
                             const int t = dx + kw;
-                            const float b = tr[g * 4 * PS + kh * G::RS + (t % PK) * G::Q + t / PK];
+                            const float b = tr[g * 4 * PS + kh * G::RSF + (t % PK) * G::QF + t / PK];
 #pragma unroll
                             for (int nt = 0; nt < 4; ++nt)
                                 acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(
@@ -269,7 +344,7 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? PS_CONV_MIN_WAVES : 1)) void c
 #pragma unroll
                 for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) best[nt][r] = fmaxf(best[nt][r], sgn * acc[nt][r]);
+                    for (int r = 0; r < 4; ++r) best[nt][r] = fmaxf(best[nt][r], acc[nt][r]);
             }
         }
 
