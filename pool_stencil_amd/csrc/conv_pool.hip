@@ -66,14 +66,15 @@ struct TileGeom {
 };
 
 // ---------------------------------------------------------------- fp32 ---
-// fp32 conv tuning: 16-byte halo loads issued per batch (bounds the registers the
-// fill holds next to the resident weights), window columns per unrolled group (0 =
-// all), and the minimum resident waves per SIMD asked of the register allocator
-// for pool windows up to 4 (three 52 KB workgroups then share a CU's LDS).  On
-// MI355X, batches of 7 with 3 waves/SIMD took the 8->64 k3 + pool-4 workload from
-// 0.745 to 0.68 ms.
+// fp32 conv tuning: tile rows a wave loads per batch (bounds the registers the fill
+// holds next to the resident weights; 12 is every row of a wave at 8 input channels
+// and pool 4), window columns per unrolled group (0 = all), and the minimum resident
+// waves per SIMD asked of the register allocator for pool windows up to 4 (three
+// 52 KB workgroups then share a CU's LDS).  On MI355X, 3 waves/SIMD took the 8->64 k3
+// + pool-4 workload from 0.745 to 0.68 ms; one batch of 12 rows instead of 7 + 5 was
+// about 4% faster again.
 #ifndef PS_CONV_FILL_BATCH
-#define PS_CONV_FILL_BATCH 7
+#define PS_CONV_FILL_BATCH 12
 #endif
 #ifndef PS_CONV_DXG
 #define PS_CONV_DXG 0
@@ -190,11 +191,11 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? PS_CONV_MIN_WAVES : 1)) void c
                 const int v = 64 * ch + lane;
                 const int ic = ic0 + 4 * v;
                 if constexpr (vec) {
-                    co[ch][0] = (ic >= 0) & (ic < W) ? 4u * (uint32_t)ic : kMasked;
+                    co[ch][0] = ((ic >= 0) & (ic < W)) ? 4u * (uint32_t)ic : kMasked;
                 } else {
 #pragma unroll
                     for (int k = 0; k < 4; ++k)
-                        co[ch][k] = (ic + k >= 0) & (ic + k < W) ? 4u * (uint32_t)(ic + k) : kMasked;
+                        co[ch][k] = ((ic + k >= 0) & (ic + k < W)) ? 4u * (uint32_t)(ic + k) : kMasked;
                 }
 #pragma unroll
                 for (int k = 0; k < 4; ++k) lw[ch][k] = col_lds(4 * v + k);
@@ -250,19 +251,24 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? PS_CONV_MIN_WAVES : 1)) void c
             constexpr int NT = 64 * NPW;
             constexpr int TOTAL = NROWS * NTAIL;
             constexpr int PER = (TOTAL + NT - 1) / NT;
-            float4 buf[PER];
+            // in batches of 7 loads (the narrow tiles run their whole fill here)
+            constexpr int TB = PER < 7 ? PER : 7;
 #pragma unroll
-            for (int i = 0; i < PER; ++i) {
+            for (int i0 = 0; i0 < PER; i0 += TB) {
+            float4 buf[TB];
+#pragma unroll
+            for (int ii = 0; ii < TB; ++ii) {
+                const int i = i0 + ii;
                 const int e = threadIdx.x + i * NT;
                 const int rr = e / NTAIL, v = 64 * NFULL + e % NTAIL;
                 const int ic = ic0 + 4 * v;
                 uint32_t ro;
-                const bool rok = (e < TOTAL) & row_in(rr, ro);
+                const bool rok = (i < PER) & (e < TOTAL) & row_in(rr, ro);
                 if constexpr (vec) {
                     const bool ok = rok & (ic >= 0) & (ic < W);
                     const uint4 q = __builtin_bit_cast(
                         uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, ok ? ro + 4u * ic : kMasked, 0, 0));
-                    buf[i] = make_float4(__uint_as_float(q.x), __uint_as_float(q.y),
+                    buf[ii] = make_float4(__uint_as_float(q.x), __uint_as_float(q.y),
                                          __uint_as_float(q.z), __uint_as_float(q.w));
                 } else {
                     float vv[4];
@@ -272,20 +278,22 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? PS_CONV_MIN_WAVES : 1)) void c
                         vv[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
                             xr, ok ? ro + 4u * (ic + k) : kMasked, 0, 0));
                     }
-                    buf[i] = make_float4(vv[0], vv[1], vv[2], vv[3]);
+                    buf[ii] = make_float4(vv[0], vv[1], vv[2], vv[3]);
                 }
             }
 #pragma unroll
-            for (int i = 0; i < PER; ++i) {
+            for (int ii = 0; ii < TB; ++ii) {
+                const int i = i0 + ii;
                 const int e = threadIdx.x + i * NT;
-                if (e < TOTAL) {
+                if (i < PER && e < TOTAL) {
                     const int rr = e / NTAIL, v = 64 * NFULL + e % NTAIL;
                     float *trow = tile + row_lds(rr);
-                    trow[col_lds(4 * v)] = buf[i].x;
-                    trow[col_lds(4 * v + 1)] = buf[i].y;
-                    trow[col_lds(4 * v + 2)] = buf[i].z;
-                    trow[col_lds(4 * v + 3)] = buf[i].w;
+                    trow[col_lds(4 * v)] = buf[ii].x;
+                    trow[col_lds(4 * v + 1)] = buf[ii].y;
+                    trow[col_lds(4 * v + 2)] = buf[ii].z;
+                    trow[col_lds(4 * v + 3)] = buf[ii].w;
                 }
+            }
             }
         }
     };
