@@ -87,7 +87,7 @@ KERNEL_SOURCES = {
     "maxpool": ["maxpool.hip", "ps_internal.h"],
     "convT": ["convt_softmax.hip", "convt_rows.hip", "ps_internal.h"],
     "conv_general": ["conv_general.hip", "ps_internal.h"],
-    "convT_bf16": ["convt_softmax_bf16.hip", "ps_internal.h"],
+    "convT_bf16": ["convt_softmax_bf16.hip", "convt_rows.hip", "ps_internal.h"],
     "maxpool_s2": ["maxpool.hip", "ps_internal.h"],
     "maxpool_d2": ["maxpool.hip", "ps_internal.h"],
     "conv_2stage": ["conv_general.hip", "two_stage.hip", "ps_internal.h"],

@@ -538,6 +538,11 @@ int launch_mt(const uint16_t *x, const uint16_t *w, const float *cb, const float
 int launch_convT_softmax_bf16(const uint16_t *x, const uint16_t *w, const float *convT_bias,
                               const float *bias2, uint16_t *y, int N, int Cin, int H, int W,
                               int Cout, int OH, int OW, int pad, float scale, hipStream_t stream) {
+    // the row-class kernel (convt_rows.hip: whole output lines per workgroup) where its
+    // envelope allows
+    const int st = launch_convT_rows_bf16(x, w, convT_bias, bias2, y, N, Cin, H, W, Cout, OH, OW,
+                                          pad, scale, stream);
+    if (st != PS_ERR_UNSUPPORTED) return st;
     switch (Cout / 32) {
         case 1: return launch_mt<1>(x, w, convT_bias, bias2, y, N, Cin, H, W, OH, OW, pad, scale, stream);
         case 2: return launch_mt<2>(x, w, convT_bias, bias2, y, N, Cin, H, W, OH, OW, pad, scale, stream);

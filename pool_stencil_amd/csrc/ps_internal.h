@@ -61,6 +61,12 @@ int launch_convT_rows(const float *x, const float *w, const float *cb, const flo
                       int N, int Cin, int H, int W, int Cout, int OH, int OW, int pad,
                       float scale, bool softmax, hipStream_t stream);
 
+// Its bf16 version (fp32 accumulation and epilogue): Cout = 128, Cin <= 64, W a
+// multiple of 8, at least 64 column positions per output row.
+int launch_convT_rows_bf16(const uint16_t *x, const uint16_t *w, const float *cb,
+                           const float *b2, uint16_t *y, int N, int Cin, int H, int W, int Cout,
+                           int OH, int OW, int pad, float scale, hipStream_t stream);
+
 // bf16 x, w and y (uint16 bit patterns), fp32 accumulation; Cout a multiple of 32.
 int launch_convT_softmax_bf16(const uint16_t *x, const uint16_t *w, const float *convT_bias,
                               const float *bias2, uint16_t *y, int N, int Cin, int H, int W,

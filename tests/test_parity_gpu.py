@@ -357,6 +357,20 @@ CONVT_BF16_CASES = [
 ]
 
 
+# the bf16 row-class kernel: Cout 128, Cin <= 64, W a multiple of 8, >= 64 column
+# positions per output row
+CONVT_BF16_ROWS_CASES = [
+    dict(N=2, Cin=64, H=5, W=64, Cout=128),
+    dict(N=1, Cin=64, H=6, W=64, Cout=128, output_padding=0),
+    dict(N=3, Cin=24, H=4, W=72, Cout=128, pad=0),
+    dict(N=2, Cin=40, H=5, W=80, Cout=128, pad=2, scale=-0.6, convT_bias=False),
+    dict(N=1, Cin=64, H=6, W=72, Cout=128, pad=3, output_padding=0),
+    dict(N=1, Cin=8, H=6, W=72, Cout=128, pad=5),
+    dict(N=64, Cin=64, H=6, W=64, Cout=128),
+]
+CONVT_BF16_CASES += CONVT_BF16_ROWS_CASES
+
+
 @pytest.mark.parametrize("kw", CONVT_BF16_CASES)
 def test_convT_bf16_small(dev, kw):
     """bf16 x/w/output: the oracle runs the fp32 definition on the bf16-rounded inputs;
