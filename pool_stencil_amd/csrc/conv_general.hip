@@ -44,6 +44,7 @@
 #include <math.h>
 
 #include <initializer_list>
+#include <type_traits>
 
 namespace ps {
 namespace {
@@ -319,53 +320,108 @@ __global__ __launch_bounds__(kThreads, 2) void conv_general(
 
         // ---- MFMA over the chunk: step = (tap, 4-channel group cq), taps outer ----
         // Operands of the next step are read from LDS while the 16 MFMAs of the
-        // current one run.  A is weight row (cq + grp)*T + tap; B is the patch at the
-        // tap's offset (the scalar state cq, tap, kw, tapoff advances with the step).
+        // current one run, into two operand sets used in turn (fp32: the loop is unrolled
+        // by two): rotating one set through the other had cost 8 register moves per step,
+        // and on this chip VALU time adds to the matrix cores' time (1.08 -> 0.94 ms on
+        // the 64 -> 128-channel workload).  A is weight row (cq + grp)*T + tap; B is the
+        // patch at the tap's offset (the scalar state cq, tap, kw, tapoff advances with
+        // the step).
         {
             const float4 *wa4 = (const float4 *)ws + grp * T * (kWRS / 4) + c;
             const float *xb = xs + grp * g.PSZ;
             const int nsteps = T * (g.CK >> 2);
             const int dstep_row = g.cd * g.IC - g.kW * g.cd;   // tapoff change at a new tap row
             int cq = 0, kw = 0, tapoff = 0, tap = 0;
-            float4 a_c = wa4[0];
-            float b_c[4];
-#pragma unroll
-            for (int tt = 0; tt < 4; ++tt) b_c[tt] = xb[off[tt]];
-            for (int st = 0;; ++st) {
-                int cq_n = cq + 4, kw_n = kw, tap_n = tapoff;
-                if (cq_n == g.CK) {
-                    cq_n = 0;
-                    ++kw_n;
-                    tap_n += g.cd;
-                    if (kw_n == g.kW) {
-                        kw_n = 0;
-                        tap_n += dstep_row;
+            auto next = [&]() {
+                cq += 4;
+                if (cq == g.CK) {
+                    cq = 0;
+                    ++tap;
+                    ++kw;
+                    tapoff += g.cd;
+                    if (kw == g.kW) {
+                        kw = 0;
+                        tapoff += dstep_row;
                     }
                 }
-                const int tap_i = cq_n == 0 ? tap + 1 : tap;
-                const bool more = st + 1 < nsteps;
-                float4 a_n = a_c;
-                float b_n[4] = {b_c[0], b_c[1], b_c[2], b_c[3]};
-                if (more) {
-                    a_n = wa4[(cq_n * T + tap_i) * (kWRS / 4)];
+            };
+            auto read_ops = [&](float4 &a, float (&b)[4]) {
+                a = wa4[(cq * T + tap) * (kWRS / 4)];
 #pragma unroll
-                    for (int tt = 0; tt < 4; ++tt) b_n[tt] = xb[cq_n * g.PSZ + tap_n + off[tt]];
-                }
-                const float av[4] = {a_c.x, a_c.y, a_c.z, a_c.w};
+                for (int tt = 0; tt < 4; ++tt) b[tt] = xb[cq * g.PSZ + tapoff + off[tt]];
+            };
+            auto mfma_step = [&](const float4 &a, const float (&b)[4]) {
+                const float av[4] = {a.x, a.y, a.z, a.w};
 #pragma unroll
                 for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
                     for (int tt = 0; tt < 4; ++tt)
                         acc[cb][tt] =
-                            __builtin_amdgcn_mfma_f32_16x16x4f32(av[cb], b_c[tt], acc[cb][tt], 0, 0, 0);
-                if (!more) break;
-                a_c = a_n;
+                            __builtin_amdgcn_mfma_f32_16x16x4f32(av[cb], b[tt], acc[cb][tt], 0, 0, 0);
+            };
+            if constexpr (sizeof(TI) == 4) {
+                float4 a0, a1;
+                float b0[4], b1[4];
+                read_ops(a0, b0);
+                for (int st = 0; st < nsteps; st += 2) {
+                    next();
+                    if (st + 1 < nsteps) read_ops(a1, b1);
+                    mfma_step(a0, b0);
+                    if (st + 1 >= nsteps) break;
+                    next();
+                    if (st + 2 < nsteps) read_ops(a0, b0);
+                    mfma_step(a1, b1);
+                }
+            } else {
+                // bf16 inputs: the one-pass fill's prefetch registers leave no room for a
+                // second operand set, so the next step's operands rotate through one
+                (void)next;
+                (void)read_ops;
+                (void)mfma_step;
+                int tap_c = 0;
+                cq = 0;
+                kw = 0;
+                tapoff = 0;
+                float4 a_c = wa4[0];
+                float b_c[4];
 #pragma unroll
-                for (int tt = 0; tt < 4; ++tt) b_c[tt] = b_n[tt];
-                cq = cq_n;
-                kw = kw_n;
-                tapoff = tap_n;
-                tap = tap_i;
+                for (int tt = 0; tt < 4; ++tt) b_c[tt] = xb[off[tt]];
+                for (int st = 0;; ++st) {
+                    int cq_n = cq + 4, kw_n = kw, tap_n = tapoff;
+                    if (cq_n == g.CK) {
+                        cq_n = 0;
+                        ++kw_n;
+                        tap_n += g.cd;
+                        if (kw_n == g.kW) {
+                            kw_n = 0;
+                            tap_n += dstep_row;
+                        }
+                    }
+                    const int tap_i = cq_n == 0 ? tap_c + 1 : tap_c;
+                    const bool more = st + 1 < nsteps;
+                    float4 a_n = a_c;
+                    float b_n[4] = {b_c[0], b_c[1], b_c[2], b_c[3]};
+                    if (more) {
+                        a_n = wa4[(cq_n * T + tap_i) * (kWRS / 4)];
+#pragma unroll
+                        for (int tt = 0; tt < 4; ++tt) b_n[tt] = xb[cq_n * g.PSZ + tap_n + off[tt]];
+                    }
+                    const float av[4] = {a_c.x, a_c.y, a_c.z, a_c.w};
+#pragma unroll
+                    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+                        for (int tt = 0; tt < 4; ++tt)
+                            acc[cb][tt] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[cb], b_c[tt],
+                                                                               acc[cb][tt], 0, 0, 0);
+                    if (!more) break;
+                    a_c = a_n;
+#pragma unroll
+                    for (int tt = 0; tt < 4; ++tt) b_c[tt] = b_n[tt];
+                    cq = cq_n;
+                    kw = kw_n;
+                    tapoff = tap_n;
+                    tap_c = tap_i;
+                }
             }
         }
     }
@@ -391,6 +447,9 @@ __global__ __launch_bounds__(kThreads, 2) void conv_general(
         const float sgn = g.scale < 0.f ? -1.f : 1.f;
         __syncthreads();                 // the region overwrites the chunk buffers
         float *ys = smem;                // [64][kYS]
+        float *lb2 = smem + kCoTile * kYS;  // [64] bias2 of the channel tile
+        if (threadIdx.x < kCoTile)
+            lb2[threadIdx.x] = ct + (int)threadIdx.x < g.Cout ? b2[ct + threadIdx.x] : 0.f;
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
@@ -407,20 +466,59 @@ __global__ __launch_bounds__(kThreads, 2) void conv_general(
                 }
             }
         __syncthreads();
-        const int ptile = g.PTH * g.PTW;
-        for (int e = threadIdx.x; e < kCoTile * ptile; e += kThreads) {
-            const int col = fdiv(e, g.mPT);
-            const int rem = e - col * ptile;
-            const int pr = fdiv(rem, g.mPTW);
-            const int pc = rem - pr * g.PTW;
-            const int co = ct + col, ph = pr0 + pr, pw = pc0 + pc;
-            if (co >= g.Cout || ph >= g.PH || pw >= g.PW) continue;
-            const float *yr = ys + col * kYS + pr * g.ps * g.CC + pc * g.ps;
-            float best = -INFINITY;
-            for (int a = 0; a < g.pk; ++a)
-                for (int bb = 0; bb < g.pk; ++bb) best = fmaxf(best, yr[a * g.pd * g.CC + bb * g.pd]);
-            const float o = best == -INFINITY ? -INFINITY : tanh_exp(sgn * best) * g.scale + b2[co];
-            store_out(y + (((size_t)n * g.Cout + co) * g.PH + ph) * g.PW + pw, o);
+        // ---- pool: thread (pooled pixel q, channel group gi) takes the pixel's window
+        // in channels [c_lo, c_hi): the window's LDS addresses are computed once and step
+        // by one region row per channel, and windows of 2-4 with dilation 1 are unrolled
+        // with immediate offsets (a per-output index decode and runtime window loops had
+        // cost about 50 VALU instructions per pooled output)
+        const int ptile = g.PTH * g.PTW;  // <= kPix: the region holds every window
+        const int ngrp = kThreads / ptile;
+        const int gi = fdiv(threadIdx.x, g.mPT);
+        const int q = threadIdx.x - gi * ptile;
+        const int pr = fdiv(q, g.mPTW), pc = q - pr * g.PTW;
+        const int ph = pr0 + pr, pw = pc0 + pc;
+        const int cpg = (kCoTile + ngrp - 1) / ngrp;
+        const int c_lo = gi * cpg;
+        const int c_hi = min(min(kCoTile, c_lo + cpg), g.Cout - ct);
+        if (gi < ngrp && ph < g.PH && pw < g.PW && c_lo < c_hi) {
+            const float *yb = ys + c_lo * kYS + pr * g.ps * g.CC + pc * g.ps;
+            TI *yp = y + (((size_t)n * g.Cout + ct + c_lo) * g.PH + ph) * g.PW + pw;
+            const size_t cstride = (size_t)g.PH * g.PW;
+            const float scale = g.scale;
+            auto finish = [&](int col, float best) {
+                const float o =
+                    best == -INFINITY ? -INFINITY : tanh_exp(sgn * best) * scale + lb2[col];
+                store_out(yp, o);
+                yp += cstride;
+            };
+            auto unrolled = [&](auto KC) {
+                constexpr int K = decltype(KC)::value;
+                for (int col = c_lo; col < c_hi; ++col, yb += kYS) {
+                    float best = -INFINITY;
+#pragma unroll
+                    for (int a = 0; a < K; ++a) {
+                        const float *row = yb + a * g.CC;
+#pragma unroll
+                        for (int bb = 0; bb < K; ++bb) best = fmaxf(best, row[bb]);
+                    }
+                    finish(col, best);
+                }
+            };
+            if (g.pd == 1 && g.pk == 3) {
+                unrolled(std::integral_constant<int, 3>{});
+            } else if (g.pd == 1 && g.pk == 2) {
+                unrolled(std::integral_constant<int, 2>{});
+            } else if (g.pd == 1 && g.pk == 4) {
+                unrolled(std::integral_constant<int, 4>{});
+            } else {
+                for (int col = c_lo; col < c_hi; ++col, yb += kYS) {
+                    float best = -INFINITY;
+                    for (int a = 0; a < g.pk; ++a)
+                        for (int bb = 0; bb < g.pk; ++bb)
+                            best = fmaxf(best, yb[a * g.pd * g.CC + bb * g.pd]);
+                    finish(col, best);
+                }
+            }
         }
     }
 }
@@ -460,7 +558,9 @@ bool plan(GenGeom &g, int epi, int &lds_bytes) {
                     if (k > cinp && k > 4) continue;
                     // patch + weights + a 64-word dummy area for the one-pass fill's stores
                     const int64_t fill = ((int64_t)k * psz + (int64_t)T * k * kWRS + 64) * 4;
-                    const int64_t need = epi == 0 && fill < kCoTile * kYS * 4 ? kCoTile * kYS * 4 : fill;
+                    // (the fused epilogue's region + bias2 reuse the chunk buffers)
+                    const int64_t epi_lds = (int64_t)kCoTile * (kYS + 1) * 4;
+                    const int64_t need = epi == 0 && fill < epi_lds ? epi_lds : fill;
                     const int64_t npr = ((int64_t)k * ir * cpl + 4 * spi - 1) / (4 * spi);
                     const int64_t nkb = ((int64_t)k * T + 15) / 16;
                     const int64_t np1 = (npr + kMaxPR - 1) / kMaxPR, np2 = (nkb + kKB - 1) / kKB;
