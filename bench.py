@@ -72,14 +72,14 @@ TINY_FLOP = 2 * 72 * 2 * 16 * 28 * 28              # the 28x28 conv outputs the 
 # x1.0.  `src` is the hash of the kernel's sources when the counters were taken; a
 # kernel edited since then reports traffic null.  See profiles/traffic_*.md.
 TRAFFIC = {
-    "conv": {"src": "641af60c69dd6ee4", "fetch_bytes": 266686969, "write_bytes": 130622224},
-    "conv_bf16": {"src": "641af60c69dd6ee4", "fetch_bytes": 136709774, "write_bytes": 80035856},
-    "maxpool": {"src": "f9f4a82d532a67be", "fetch_bytes": 2160264222, "write_bytes": 2140716768},
-    "maxpool_s2": {"src": "f9f4a82d532a67be", "fetch_bytes": 2176869184, "write_bytes": 536870912},
-    "maxpool_d2": {"src": "f9f4a82d532a67be", "fetch_bytes": 2266858564, "write_bytes": 2147483648},
-    "convT": {"src": "333c26b93de1daf3", "fetch_bytes": 604640218, "write_bytes": 2347717312},
-    "convT_bf16": {"src": "68ece0f4911cfb2c", "fetch_bytes": 119831797, "write_bytes": 590689392},
-    "conv_general": {"src": "a6c2d8a9bfe78480", "fetch_bytes": 136918791, "write_bytes": 69311232},
+    "conv": {"src": "7b780394d52d24f2", "fetch_bytes": 266689368, "write_bytes": 130635600},
+    "conv_bf16": {"src": "7b780394d52d24f2", "fetch_bytes": 136705727, "write_bytes": 80952688},
+    "maxpool": {"src": "628c5336c160dc49", "fetch_bytes": 2160264739, "write_bytes": 2140759792},
+    "maxpool_s2": {"src": "628c5336c160dc49", "fetch_bytes": 2176856395, "write_bytes": 536870912},
+    "maxpool_d2": {"src": "628c5336c160dc49", "fetch_bytes": 2266403326, "write_bytes": 2147483648},
+    "convT": {"src": "5874c50cc83a0238", "fetch_bytes": 139921047, "write_bytes": 1252181584},
+    "convT_bf16": {"src": "4c8a7b3c3b752233", "fetch_bytes": 78062438, "write_bytes": 771616432},
+    "conv_general": {"src": "bd29c32b501c5d67", "fetch_bytes": 137108786, "write_bytes": 69146448},
 }
 KERNEL_SOURCES = {
     "conv": ["conv_pool.hip", "ps_internal.h"],
