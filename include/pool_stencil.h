@@ -75,8 +75,8 @@ int ps_version(void);
 
 /* ---------------------------------------------------------------- shapes --- */
 /* Pure host arithmetic; no device needed.  Writes *out and returns PS_OK, or
- * returns PS_ERR_PARAM (k,s,d < 1 or p < 0) / PS_ERR_SHAPE (in < 1 or the
- * result < 1) and leaves *out untouched. */
+ * returns PS_ERR_PARAM (k,s,d < 1 or p < 0) / PS_ERR_SHAPE (in < 1, or the
+ * result < 1 or above INT_MAX) and leaves *out untouched. */
 int ps_conv2d_out_dim(int in, int k, int stride, int pad, int dil, int *out);
 /* MaxPool2d, floor mode; stride <= 0 means stride = k (nn.MaxPool2d's default). */
 int ps_pool2d_out_dim(int in, int k, int stride, int pad, int dil, int *out);

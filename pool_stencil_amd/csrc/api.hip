@@ -56,7 +56,7 @@ int ps_conv2d_out_dim(int in, int k, int stride, int pad, int dil, int *out) {
     if (k < 1 || stride < 1 || dil < 1 || pad < 0) return PS_ERR_PARAM;
     if (in < 1) return PS_ERR_SHAPE;
     const int64_t o = window_extent(in, k, stride, pad, dil);
-    if (o < 1) return PS_ERR_SHAPE;
+    if (o < 1 || o > 0x7fffffff) return PS_ERR_SHAPE;  // (an extent past INT_MAX: no int)
     *out = (int)o;
     return PS_OK;
 }
