@@ -80,6 +80,10 @@ TRAFFIC = {
     "convT": {"src": "5874c50cc83a0238", "fetch_bytes": 139921047, "write_bytes": 1252181584},
     "convT_bf16": {"src": "4c8a7b3c3b752233", "fetch_bytes": 78062438, "write_bytes": 771616432},
     "conv_general": {"src": "bd29c32b501c5d67", "fetch_bytes": 137108786, "write_bytes": 69146448},
+    "conv_2stage#0": {"src": "4670a80cc2d7d8f1", "fetch_bytes": 270086315, "write_bytes": 2115119536},
+    "conv_2stage#1": {"src": "4670a80cc2d7d8f1", "fetch_bytes": 2104812003, "write_bytes": 152451056},
+    "convT_2stage#0": {"src": "4f981781a6eb6c82", "fetch_bytes": 138904441, "write_bytes": 1294380208},
+    "convT_2stage#1": {"src": "4f981781a6eb6c82", "fetch_bytes": 1223745874, "write_bytes": 1121292928},
 }
 KERNEL_SOURCES = {
     "conv": ["conv_pool.hip", "ps_internal.h"],
@@ -105,8 +109,9 @@ def source_hash(op):
 
 
 def traffic(op):
+    """HBM bytes per launch of `op` (a stage of a two-stage op is "name#i"), or None."""
     t = TRAFFIC.get(op)
-    if not t or t["src"] != source_hash(op):
+    if not t or t["src"] != source_hash(op.split("#")[0]):
         return None
     return t["fetch_bytes"] + t["write_bytes"]
 
@@ -374,10 +379,12 @@ def main():
             "ms_mean": m0 + m1, "stage_ms": [m0, m1],
             "fusion_speedup": (m0 + m1) / fused if fused else None,
             "roofline": {"bound": "mfma", "achieved": a0 / 1e12, "peak": PEAK_FP32 / 1e12,
-                         "unit": "TFLOP/s", "frac": a0 / PEAK_FP32, "traffic": None,
+                         "unit": "TFLOP/s", "frac": a0 / PEAK_FP32,
+                         "traffic": traffic("conv_2stage#0"),
                          "kernel": "conv2d stage (76.1 GFLOP over all 254x254 outputs)"},
             "stage2_roofline": {"bound": "hbm", "achieved": b1 / 1e9, "peak": PEAK_HBM / 1e9,
-                                "unit": "GB/s", "frac": b1 / PEAK_HBM}}
+                                "unit": "GB/s", "frac": b1 / PEAK_HBM,
+                                "traffic": traffic("conv_2stage#1")}}
     if "convT_2stage#0" in runs:
         m0, m1 = stats("convT_2stage#0")[0], stats("convT_2stage#1")[0]
         a0 = CONVT_FLOP / (m0 * 1e-3)
@@ -388,10 +395,11 @@ def main():
             "ms_mean": m0 + m1, "stage_ms": [m0, m1],
             "fusion_speedup": (m0 + m1) / fused if fused else None,
             "roofline": {"bound": "mfma", "achieved": a0 / 1e12, "peak": PEAK_FP32 / 1e12,
-                         "unit": "TFLOP/s", "frac": a0 / PEAK_FP32, "traffic": None,
-                         "kernel": "convT stage"},
+                         "unit": "TFLOP/s", "frac": a0 / PEAK_FP32,
+                         "traffic": traffic("convT_2stage#0"), "kernel": "convT stage"},
             "stage2_roofline": {"bound": "hbm", "achieved": b1 / 1e9, "peak": PEAK_HBM / 1e9,
-                                "unit": "GB/s", "frac": b1 / PEAK_HBM}}
+                                "unit": "GB/s", "frac": b1 / PEAK_HBM,
+                                "traffic": traffic("convT_2stage#1")}}
 
     if "tiny_conv" in runs:
         mean, med, mn = stats("tiny_conv")
