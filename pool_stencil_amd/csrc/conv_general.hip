@@ -426,6 +426,25 @@ __global__ __launch_bounds__(kThreads, 2) void conv_general(
         }
     }
 
+    // conv bias of D row 4*grp + r of block cb (channel ct + 16cb + 4grp + r): the 16
+    // loads at clamped indices, all in flight together (a conditional load per channel
+    // had compiled to a branch and a wait each)
+    float cbv[4][4];
+    if (cbias) {
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int co = ct + 16 * cb + 4 * grp + r;
+                cbv[cb][r] = cbias[co < g.Cout ? co : 0];
+            }
+    } else {
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) cbv[cb][r] = 0.f;
+    }
+
     if constexpr (EPI == 1) {
         // ---- plain conv: D row 4*grp + r of block cb is channel ct + 16cb + 4grp + r ----
         const size_t oplane = (size_t)g.OH * g.OW;
@@ -435,7 +454,7 @@ __global__ __launch_bounds__(kThreads, 2) void conv_general(
             for (int r = 0; r < 4; ++r) {
                 const int co = ct + 16 * cb + 4 * grp + r;
                 if (co >= g.Cout) continue;
-                const float bias = cbias ? cbias[co] : 0.f;
+                const float bias = cbv[cb][r];
                 TI *yp = y + ((size_t)n * g.Cout + co) * oplane;
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt)
@@ -455,8 +474,7 @@ __global__ __launch_bounds__(kThreads, 2) void conv_general(
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int col = 16 * cb + 4 * grp + r;
-                const int co = ct + col;
-                const float bias = (cbias && co < g.Cout) ? cbias[co] : 0.f;
+                const float bias = cbv[cb][r];
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt) {
                     const int p = 16 * (wv + 4 * tt) + c;

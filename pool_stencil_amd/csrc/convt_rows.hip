@@ -48,7 +48,6 @@ namespace {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 512;  // 8 waves, two per SIMD
@@ -69,11 +68,6 @@ __device__ __forceinline__ float quad_xor1(float v) {
 }
 __device__ __forceinline__ float quad_xor2(float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
-}
-// DPP row_half_mirror: lane i of each group of 8 takes lane 7 - i (after the two quad
-// steps, this completes a reduction over the 8 lanes)
-__device__ __forceinline__ float half_mirror(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
 }
 
 struct RowsGeom {
@@ -433,19 +427,10 @@ __global__ __launch_bounds__(kThreads) void convT_rows_f32(
 //     channel pairs (16 pad bytes per column), so a lane's B operand is one 16-byte read;
 //   - the accumulators start at the convT bias; log2 e is applied inside the softmax's
 //     fma (scaling the bf16 weights would round them);
-//   - epilogue thread (position, channel group of 16) holds both columns of the
-//     position, so each output pair of columns is rounded to bf16 (nearest even) by one
-//     packed conversion and written by one 4-byte range-checked buffer store (a pair
-//     with one column outside the row is written as a 2-byte store); the stores of a
-//     tile are issued a few at a time between the next tile's K-steps.
+//   - outputs are rounded to bf16 (nearest even) and stored as 2-byte range-checked
+//     buffer stores.
 constexpr int kThreadsB = 256;  // 4 waves x 32 channels
 constexpr int kTPB = 32;        // positions per bf16 tile: 2 blocks of 16
-// bf16 epilogue exchange: slot (32 b' + position) of kESB words, channel c at word
-// 20 (c / 16) + c mod 16.  The slot stride (4 mod 32 words) keeps 8 neighbouring
-// positions' 16-byte writes on distinct banks, the 20-word channel groups keep the 8
-// channel groups' 16-byte reads of one position on distinct banks.
-constexpr int kESB = 164;
-__host__ __device__ constexpr int exb_word(int c) { return 20 * (c >> 4) + (c & 15); }
 
 template <int CB>  // input-channel blocks of 32: Cin <= 32 * CB
 __global__ __launch_bounds__(kThreadsB, 2) void convT_rows_bf16(
@@ -457,9 +442,8 @@ __global__ __launch_bounds__(kThreadsB, 2) void convT_rows_bf16(
     constexpr int CSTW = 16 * CB + 4;  // LDS words per ring column: 32*CB channels + 16 bytes
     const int slot_words = (Cpos + 1) * CSTW;
     uint32_t *ring = (uint32_t *)lds;         // [kRing][Cpos + 1][CSTW] channel-pair words
-    float *ex = lds + kRing * slot_words;     // [2 * kTPB slots][kESB]
-    float *lb2 = ex + 2 * kTPB * kESB;        // [kCout] -bias2 * scale * log2 e
-    uint32_t *dummy = (uint32_t *)(lb2 + kCout);  // [64] fill writes with no place in the ring
+    float *ex = lds + kRing * slot_words;     // [2 * kTPB pairs][kES]
+    float *lb2 = ex + 2 * kTPB * kES;         // [kCout] -bias2 * scale * log2 e
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -533,25 +517,21 @@ __global__ __launch_bounds__(kThreadsB, 2) void convT_rows_bf16(
 #pragma unroll
     for (int k = 0; k < 8; ++k)
         if (f_on && f_j0 + k >= 0 && f_j0 + k <= Cpos) f_m |= 1 << k;
-    // unconditional and branch-free, as in the fp32 kernel (a row that is not needed
-    // reads zeros and goes to a per-lane dummy word)
-    uint32_t *const dl = dummy + lane;
-    auto fill_load = [&](int ih, bool on, u32x4 (&v)[2]) {
-        const bool rin = on && ih >= 0 && ih < H;
+    auto fill_load = [&](int ih, u32x4 (&v)[2]) {
+        const bool rin = ih >= 0 && ih < H;
         const uint32_t ro = 2u * (uint32_t)(rin ? ih : 0) * W;
 #pragma unroll
         for (int h = 0; h < 2; ++h)
             v[h] = __builtin_amdgcn_raw_buffer_load_b128(xr, rin ? fo[h] + ro : kMasked, 0, 0);
     };
     // word k of the slot column: the bf16 of column k of both channels (byte permute)
-    auto fill_store = [&](int ih, bool on, const u32x4 (&v)[2]) {
+    auto fill_store = [&](int ih, const u32x4 (&v)[2]) {
         uint32_t *dst = ring + ((ih + 1) & (kRing - 1)) * slot_words + f_j0 * CSTW + f_cp;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            uint32_t *d = on && (f_m & (1 << k)) ? dst + k * CSTW : dl;
-            *d = __builtin_amdgcn_perm(v[1][k >> 1], v[0][k >> 1],
-                                       (k & 1) ? 0x07060302u : 0x05040100u);
-        }
+        for (int k = 0; k < 8; ++k)
+            if (f_m & (1 << k))
+                dst[k * CSTW] = __builtin_amdgcn_perm(v[1][k >> 1], v[0][k >> 1],
+                                                      (k & 1) ? 0x07060302u : 0x05040100u);
     };
     auto tile_rows = [&](int T, int &lo, int &hi) {
         const int t0 = T * kTPB;
@@ -568,8 +548,8 @@ __global__ __launch_bounds__(kThreadsB, 2) void convT_rows_bf16(
     tile_rows(T0, lo, hi);
     for (int ih = lo; ih <= hi; ++ih) {
         u32x4 v[2];
-        fill_load(ih, true, v);
-        fill_store(ih, true, v);
+        fill_load(ih, v);
+        fill_store(ih, v);
     }
     __syncthreads();
 
@@ -585,18 +565,16 @@ __global__ __launch_bounds__(kThreadsB, 2) void convT_rows_bf16(
         pm[bk] = (int)fdiv(t, geo.mC);
         pc[bk] = (int)t - pm[bk] * Cpos;
     }
-    // epilogue: thread (position pe, channel group cg) owns channels 16cg .. 16cg+15 of
-    // both columns of position pe; the 8 channel groups of a position are 8 neighbouring
-    // lanes
-    const int pe = tid >> 3, cg = tid & 7;
+    // epilogue: thread (pair p, channel quarter cq), pair p = 2 * (position) + b'
+    const int p = tid >> 2, cq = tid & 3;
     int em, ec;
     {
-        const uint32_t t = (uint32_t)(T0 * kTPB + pe);
+        const uint32_t t = (uint32_t)(T0 * kTPB + (p >> 1));
         em = (int)fdiv(t, geo.mC);
         ec = (int)t - em * Cpos;
     }
-    // output row index (n, channel 16cg, row class a) at position row 0 (below 2^24)
-    const uint32_t yrow0 = __umul24((uint32_t)n * kCout + 16 * cg, (uint32_t)OH) + a;
+    // output row index (n, channel 32cq, row class a) at position row 0 (below 2^24)
+    const uint32_t yrow0 = __umul24((uint32_t)n * kCout + 32 * cq, (uint32_t)OH) + a;
 
     // next tile's new row loaded one tile ahead, before the stores (as in the fp32 kernel)
     u32x4 pv[2];
@@ -606,20 +584,23 @@ __global__ __launch_bounds__(kThreadsB, 2) void convT_rows_bf16(
         tile_rows(T0 + 1, nlo, nhi);
     }
     bool has_new = nhi > hi;
-    fill_load(nhi, has_new, pv);
+    if (has_new) fill_load(nhi, pv);
 
-    // The previous tile's outputs (word i: channel 16cg + i, both columns as bf16) and
-    // their byte offset; stored a few at a time between the next tile's K-steps, so the
-    // stores drain beside the matrix work instead of in one burst per tile.
+    // The previous tile's outputs (bf16 pairs: channels 2i, 2i + 1 of the lane's 32) and
+    // their offset; stored a few at a time between the next tile's K-steps, so the stores
+    // drain beside the matrix work instead of in one burst per tile.
     uint32_t pend[16];
     uint32_t pyo = kMasked;
 #pragma unroll
     for (int i = 0; i < 16; ++i) pend[i] = 0u;
     auto store_pend = [&](int i0, int cnt) {
 #pragma unroll
-        for (int i = i0; i < i0 + cnt; ++i)
-            __builtin_amdgcn_raw_buffer_store_b32(pend[i], yr, pyo,
-                                                  (int)(2u * (uint32_t)i * oplane), 0);
+        for (int i = i0; i < i0 + cnt; ++i) {
+            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)pend[i], yr, pyo,
+                                                  (int)(2u * (uint32_t)(2 * i) * oplane), 0);
+            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(pend[i] >> 16), yr, pyo,
+                                                  (int)(2u * (uint32_t)(2 * i + 1) * oplane), 0);
+        }
     };
 
     for (int T = T0; T < T1; ++T) {
@@ -657,10 +638,8 @@ __global__ __launch_bounds__(kThreadsB, 2) void convT_rows_bf16(
 #pragma unroll
                 for (int bk = 0; bk < 2; ++bk) bv[(st + 1) & 1][bk] = read_b(bk, st + 1);
             }
-            // the previous tile's stores, 16 / (4 CB) per step (dropped before the first
-            // tile: pyo is masked; issuing them keeps the compiler's count of memory
-            // operations in flight exact, so the ring write below waits for its loads only)
-            store_pend(st * (4 / CB), 4 / CB);
+            // the previous tile's stores, 16 / (4 CB) pairs per step (none before the first)
+            if (T > T0) store_pend(st * (4 / CB), 4 / CB);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int bk = 0; bk < 2; ++bk)
@@ -673,7 +652,7 @@ __global__ __launch_bounds__(kThreadsB, 2) void convT_rows_bf16(
             __builtin_amdgcn_sched_barrier(0);
         }
 
-        fill_store(nhi, has_new, pv);
+        if (has_new) fill_store(nhi, pv);
         hi = nhi;
 #pragma unroll
         for (int bk = 0; bk < 2; ++bk) {
@@ -690,93 +669,69 @@ __global__ __launch_bounds__(kThreadsB, 2) void convT_rows_bf16(
             for (int b = 0; b < 2; ++b)
 #pragma unroll
                 for (int bk = 0; bk < 2; ++bk)
-                    *(f32x4 *)(ex + (32 * b + 16 * bk + j) * kESB +
-                               exb_word(32 * wv + 16 * ct) + 4 * g) = acc[ct][b][bk];
+                    *(f32x4 *)(ex + (2 * (16 * bk + j) + b) * kES + 32 * wv + 16 * ct + 4 * g) =
+                        acc[ct][b][bk];
         __syncthreads();  // exchange complete, and the ring holds the next tile's rows
 
-        // ---- epilogue: 16 channels of both columns of one position
-        const int ow0 = 2 * ec + d0;  // column of b' = 0
-        const bool pin = em < Mc;
-        const bool lo_ok = pin && ow0 >= 0 && ow0 < OW;
-        const bool hi_ok = pin && ow0 + 1 < OW;  // (ow0 + 1 >= 0 always)
-        const uint32_t po = 2u * (__umul24(yrow0 + 2u * (uint32_t)em, (uint32_t)OW) + (uint32_t)ow0);
-        ec += kTPB;
-        if (ec >= Cpos) {
-            ec -= Cpos;
-            ++em;
-        }
-        float v0[16], v1[16];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const f32x4 t0 = *(const f32x4 *)(ex + pe * kESB + exb_word(16 * cg) + 4 * r);
-            const f32x4 t1 = *(const f32x4 *)(ex + (32 + pe) * kESB + exb_word(16 * cg) + 4 * r);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                v0[4 * r + i] = t0[i];
-                v1[4 * r + i] = t1[i];
+        // ---- epilogue: 32 channels of one pair
+        uint32_t yo;
+        {
+            const int ow = 2 * ec + d0 + (p & 1);
+            const bool ok = em < Mc && ow >= 0 && ow < OW;
+            yo = ok ? 2u * (__umul24(yrow0 + 2u * (uint32_t)em, (uint32_t)OW) + (uint32_t)ow)
+                    : kMasked;
+            ec += kTPB;
+            if (ec >= Cpos) {
+                ec -= Cpos;
+                ++em;
             }
+        }
+        float v[32];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const f32x4 t = *(const f32x4 *)(ex + p * kES + 32 * cq + 4 * r);
+            v[4 * r] = t[0];
+            v[4 * r + 1] = t[1];
+            v[4 * r + 2] = t[2];
+            v[4 * r + 3] = t[3];
         }
         // e_c = 2^((t_c - max) log2 e), out_c = 1 / (1 + 2^(e_c * inv + b2'_c)),
         // inv = -scale * log2 e / sum_c e_c, b2'_c = -bias2_c * scale * log2 e
-        float mx0 = v0[0], mx1 = v1[0];
+        float mx = v[0];
 #pragma unroll
-        for (int r = 1; r < 16; ++r) {
-            mx0 = fmaxf(mx0, v0[r]);
-            mx1 = fmaxf(mx1, v1[r]);
+        for (int r = 1; r < 32; ++r) mx = fmaxf(mx, v[r]);
+        mx = fmaxf(mx, quad_xor1(mx));
+        mx = fmaxf(mx, quad_xor2(mx));
+        const float nmx = -mx * kLog2e;
+        float sum = 0.f;
+#pragma unroll
+        for (int r = 0; r < 32; ++r) {
+            v[r] = __builtin_amdgcn_exp2f(fmaf(v[r], kLog2e, nmx));
+            sum += v[r];
         }
-        mx0 = fmaxf(mx0, quad_xor1(mx0));
-        mx1 = fmaxf(mx1, quad_xor1(mx1));
-        mx0 = fmaxf(mx0, quad_xor2(mx0));
-        mx1 = fmaxf(mx1, quad_xor2(mx1));
-        mx0 = fmaxf(mx0, half_mirror(mx0));
-        mx1 = fmaxf(mx1, half_mirror(mx1));
-        const float nmx0 = -mx0 * kLog2e, nmx1 = -mx1 * kLog2e;
-        float sum0 = 0.f, sum1 = 0.f;
+        sum += quad_xor1(sum);
+        sum += quad_xor2(sum);
+        const float inv = -scale * kLog2e * __builtin_amdgcn_rcpf(sum);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            v0[r] = __builtin_amdgcn_exp2f(fmaf(v0[r], kLog2e, nmx0));
-            v1[r] = __builtin_amdgcn_exp2f(fmaf(v1[r], kLog2e, nmx1));
-            sum0 += v0[r];
-            sum1 += v1[r];
-        }
-        sum0 += quad_xor1(sum0);
-        sum1 += quad_xor1(sum1);
-        sum0 += quad_xor2(sum0);
-        sum1 += quad_xor2(sum1);
-        sum0 += half_mirror(sum0);
-        sum1 += half_mirror(sum1);
-        const float inv0 = -scale * kLog2e * __builtin_amdgcn_rcpf(sum0);
-        const float inv1 = -scale * kLog2e * __builtin_amdgcn_rcpf(sum1);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const f32x4 bb = *(const f32x4 *)(lb2 + 16 * cg + 4 * r);
+        for (int r = 0; r < 8; ++r) {
+            const f32x4 bb = *(const f32x4 *)(lb2 + 32 * cq + 4 * r);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float t0 = __builtin_amdgcn_exp2f(fmaf(v0[4 * r + i], inv0, bb[i]));
-                const float t1 = __builtin_amdgcn_exp2f(fmaf(v1[4 * r + i], inv1, bb[i]));
-                const f32x2 o = {__builtin_amdgcn_rcpf(1.f + t0), __builtin_amdgcn_rcpf(1.f + t1)};
-                // both columns rounded to bf16 (nearest even) by one packed conversion
-                pend[4 * r + i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(o, bf16x2));
+                const float t = __builtin_amdgcn_exp2f(fmaf(v[4 * r + i], inv, bb[i]));
+                v[4 * r + i] = __builtin_amdgcn_rcpf(1.f + t);
             }
         }
-        pyo = lo_ok && hi_ok ? po : kMasked;
-        if (lo_ok != hi_ok) {
-            // one column of the pair lies outside the row: that column alone, now
-            const uint32_t eo = lo_ok ? po : po + 2u;
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                __builtin_amdgcn_raw_buffer_store_b16(
-                    (uint16_t)(lo_ok ? pend[i] : pend[i] >> 16), yr, eo,
-                    (int)(2u * (uint32_t)i * oplane), 0);
-        }
-        // the row tile T + 2 adds, loaded after this tile's stores so far (at the ring
-        // write only the tile's pipelined stores are younger than it)
         if (T + 2 < T1) {
             int nlo;
             tile_rows(T + 2, nlo, nhi);
         }
         has_new = nhi > hi;
-        fill_load(nhi, has_new, pv);
+        if (has_new) fill_load(nhi, pv);
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            pend[i] = (uint32_t)f32_to_bf16_rne(v[2 * i]) |
+                      ((uint32_t)f32_to_bf16_rne(v[2 * i + 1]) << 16);
+        pyo = yo;
     }
     store_pend(0, 16);  // the last tile's outputs
 }
@@ -867,7 +822,7 @@ int launch_convT_rows_bf16(const uint16_t *x, const uint16_t *w, const float *cb
     if (geo.Cpos < kTP) return PS_ERR_UNSUPPORTED;
     const int CB = (Cin + 31) / 32;
     const size_t lds_words =
-        (size_t)kRing * (geo.Cpos + 1) * (16 * CB + 4) + 2 * kTPB * kESB + kCout + 64;
+        (size_t)kRing * (geo.Cpos + 1) * (16 * CB + 4) + 2 * kTPB * kES + kCout;
     if (lds_words * 4 > 160 * 1024) return PS_ERR_UNSUPPORTED;
     if ((int64_t)2 * N * Cin * H * W >= (1ll << 31) ||
         (int64_t)2 * N * kCout * OH * OW >= (1ll << 31) ||
