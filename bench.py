@@ -72,18 +72,18 @@ TINY_FLOP = 2 * 72 * 2 * 16 * 28 * 28              # the 28x28 conv outputs the 
 # x1.0.  `src` is the hash of the kernel's sources when the counters were taken; a
 # kernel edited since then reports traffic null.  See profiles/traffic_*.md.
 TRAFFIC = {
-    "conv": {"src": "7b780394d52d24f2", "fetch_bytes": 266689368, "write_bytes": 130635600},
-    "conv_bf16": {"src": "7b780394d52d24f2", "fetch_bytes": 136705727, "write_bytes": 80952688},
-    "maxpool": {"src": "628c5336c160dc49", "fetch_bytes": 2160264739, "write_bytes": 2140759792},
-    "maxpool_s2": {"src": "628c5336c160dc49", "fetch_bytes": 2176856395, "write_bytes": 536870912},
-    "maxpool_d2": {"src": "628c5336c160dc49", "fetch_bytes": 2266403326, "write_bytes": 2147483648},
-    "convT": {"src": "5874c50cc83a0238", "fetch_bytes": 139921047, "write_bytes": 1252181584},
-    "convT_bf16": {"src": "4c8a7b3c3b752233", "fetch_bytes": 78062438, "write_bytes": 771616432},
-    "conv_general": {"src": "bd29c32b501c5d67", "fetch_bytes": 137108786, "write_bytes": 69146448},
-    "conv_2stage#0": {"src": "4670a80cc2d7d8f1", "fetch_bytes": 270086315, "write_bytes": 2115119536},
-    "conv_2stage#1": {"src": "4670a80cc2d7d8f1", "fetch_bytes": 2104812003, "write_bytes": 152451056},
-    "convT_2stage#0": {"src": "4f981781a6eb6c82", "fetch_bytes": 138904441, "write_bytes": 1294380208},
-    "convT_2stage#1": {"src": "4f981781a6eb6c82", "fetch_bytes": 1223745874, "write_bytes": 1121292928},
+    "conv": {"src": "7b780394d52d24f2", "fetch_bytes": 266688843, "write_bytes": 130641104},
+    "conv_bf16": {"src": "7b780394d52d24f2", "fetch_bytes": 136705458, "write_bytes": 80347680},
+    "maxpool": {"src": "628c5336c160dc49", "fetch_bytes": 2160260234, "write_bytes": 2140746016},
+    "maxpool_s2": {"src": "628c5336c160dc49", "fetch_bytes": 2176863633, "write_bytes": 536870912},
+    "maxpool_d2": {"src": "628c5336c160dc49", "fetch_bytes": 2266848453, "write_bytes": 2147483648},
+    "convT": {"src": "19452b55b8ce8c8c", "fetch_bytes": 141140378, "write_bytes": 1260160384},
+    "convT_bf16": {"src": "6e57bf9ac0b37673", "fetch_bytes": 77817876, "write_bytes": 772167728},
+    "conv_general": {"src": "456ad05d0ed2d488", "fetch_bytes": 137133028, "write_bytes": 69415152},
+    "conv_2stage#0": {"src": "8cfb246101a56548", "fetch_bytes": 277502105, "write_bytes": 2116773216},
+    "conv_2stage#1": {"src": "8cfb246101a56548", "fetch_bytes": 2104807670, "write_bytes": 152430560},
+    "convT_2stage#0": {"src": "3f02b739b4f13100", "fetch_bytes": 140682282, "write_bytes": 1296515872},
+    "convT_2stage#1": {"src": "3f02b739b4f13100", "fetch_bytes": 1223737195, "write_bytes": 1121207536},
 }
 KERNEL_SOURCES = {
     "conv": ["conv_pool.hip", "ps_internal.h"],

@@ -207,12 +207,9 @@ __global__ __launch_bounds__(kThreads) void convT_rows_f32(
         hi = (int)fdiv((uint32_t)t1, geo.mC) + ra;
     };
 
-    // Workgroups start staggered over about one tile (eight groups of about 1.7 us).
-    // Started together, every CU reaches its epilogue and output stores at the same
-    // moment and the chip's stores arrive in bursts at the HBM write limit (1.40 ->
-    // 1.26 ms).  Row class 1, which has one position row less when OH is odd, takes
-    // the later half, so the delay does not lengthen the longest workgroup (-> 1.19 ms).
-    for (int i = 0; i < (int)((L >> 1) & 3) + 4 * a; ++i) __builtin_amdgcn_s_sleep(64);
+    // (No start stagger: while each tile's ring write waited for all of the tile's
+    // output stores, staggered starts kept the chip's stores from arriving in bursts;
+    // with the exact wait it no longer pays.)
     __syncthreads();  // ring zeroed before the first fill writes into it
     if (T0 >= T1) return;
     int lo, hi;
@@ -540,7 +537,9 @@ __global__ __launch_bounds__(kThreadsB, 2) void convT_rows_bf16(
         hi = (int)fdiv((uint32_t)t1, geo.mC) + ra;
     };
 
-    // start stagger as in the fp32 kernel
+    // Workgroups start in eight groups about 0.85 us apart (row class 1, one position
+    // row shorter when OH is odd, in the later four), so the chip's output stores do
+    // not all arrive in the same bursts.
     for (int i = 0; i < (int)((L >> 1) & 3) + 4 * a; ++i) __builtin_amdgcn_s_sleep(32);
     __syncthreads();
     if (T0 >= T1) return;
