@@ -90,7 +90,7 @@ __global__ __launch_bounds__(kThreads) void convT_rows_f32(
     constexpr int CST = 16 * CQ + 4;  // LDS words per ring column (channels padded)
     const int slot_words = (Cpos + 1) * CST;
     float *ring = lds;                          // [kRing][Cpos + 1][CST]
-    float *ex = lds + kRing * slot_words;       // [2 * kTP pairs][kES]
+    float *ex = lds + kRing * slot_words;       // [2 * kTP pairs][kES], swizzled (ex_quad)
     float *lcb = ex + 2 * kTP * kES;            // [kCout] convT bias (times log2 e with the softmax)
     float *lb2 = lcb + kCout;                   // [kCout] -bias2 * scale * log2 e
     float *dummy = lb2 + kCout;                 // [64][2] fill writes with no place in the ring
@@ -251,6 +251,19 @@ __global__ __launch_bounds__(kThreads) void convT_rows_f32(
     // 2^22 (y below 2^29 elements, OW >= 127), so 24-bit multiplies are exact
     const uint32_t yrow0 = __umul24((uint32_t)n * kCout + 32 * cq, (uint32_t)OH) + a;
 
+    // Exchange layout: pair p's slot holds channel quad C (channels 4C .. 4C+3) at quad
+    // ex_quad(p, C).  With this swizzle the D-tile writes (16 positions of one column
+    // class per 16 lanes) and the epilogue reads (two pairs x four channel quarters per
+    // 8 lanes) hit 8 distinct 16-byte bank groups; unswizzled, the writes were 2-way and
+    // the reads 4-way bank conflicts.
+    auto ex_quad = [](int pair, int C) { return (C ^ ((C >> 2) & 6)) ^ ((pair >> 1) & 15); };
+    // this lane's D-tile write: pair 2(16 bk + j) + b, whose (pair >> 1) & 15 is j
+    const int ex_w = 2 * j * kES + 4 * ((4 * wv + g) ^ (((4 * wv + g) >> 2) & 6) ^ j);
+    // this lane's 8 epilogue reads, channel quads 8 cq + r
+    int ex_r[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) ex_r[r] = p * kES + 4 * ex_quad(p, 8 * cq + r);
+
     // The next tile's new input row (at most one: a tile spans at most two position
     // rows) is loaded one tile ahead, before the current tile's output stores: queued
     // behind those stores, the load held the wave's in-order issue until they drained.
@@ -341,7 +354,7 @@ __global__ __launch_bounds__(kThreads) void convT_rows_f32(
         for (int b = 0; b < 2; ++b)
 #pragma unroll
             for (int bk = 0; bk < 4; ++bk)
-                *(f32x4 *)(ex + (2 * (16 * bk + j) + b) * kES + 16 * wv + 4 * g) = acc[b][bk];
+                *(f32x4 *)(ex + (32 * bk + b) * kES + ex_w) = acc[b][bk];
         __syncthreads();  // exchange complete, and the ring holds the next tile's rows
 
         // ---- epilogue
@@ -360,7 +373,7 @@ __global__ __launch_bounds__(kThreads) void convT_rows_f32(
         float v[32];
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-            const f32x4 t = *(const f32x4 *)(ex + p * kES + 32 * cq + 4 * r);
+            const f32x4 t = *(const f32x4 *)(ex + ex_r[r]);
             v[4 * r] = t[0];
             v[4 * r + 1] = t[1];
             v[4 * r + 2] = t[2];
