@@ -124,12 +124,15 @@ def test_tanh_scale_bias_maxpool_small(dev, case, dtype):
 
 
 # ------------------------------------------- softmax post-process of a convT ---
-@pytest.mark.parametrize("C", [8, 48, 128, 130, 200])
+@pytest.mark.parametrize("C,H,W", [(8, 9, 13), (48, 9, 13), (128, 9, 13), (130, 9, 13),
+                                   (200, 9, 13), (128, 17, 19), (128, 16, 16)])
 @pytest.mark.parametrize("inplace", [False, True])
-def test_softmax_bias_scale_sigmoid_small(dev, C, inplace):
+def test_softmax_bias_scale_sigmoid_small(dev, C, H, W, inplace):
+    """Channel counts up to 128 keep a pixel's channels in registers, more take two
+    passes; the 128-channel shapes cover one, several and ragged 256-pixel blocks."""
     import pool_stencil_amd as ps
-    _say("softmax_bias_scale_sigmoid", C, "inplace" if inplace else "", "seed 7200")
-    y = inputgen.randn(7200, (2, C, 9, 13), 3.0)
+    _say("softmax_bias_scale_sigmoid", C, H, W, "inplace" if inplace else "", "seed 7200")
+    y = inputgen.randn(7200, (2, C, H, W), 3.0)
     b2 = inputgen.randn(7201, (C,), 0.1)
     ref = oracle.softmax_bias_scale_sigmoid(y, b2, -0.8)
     yd = _dev(y, dev)
