@@ -72,18 +72,18 @@ TINY_FLOP = 2 * 72 * 2 * 16 * 28 * 28              # the 28x28 conv outputs the 
 # x1.0.  `src` is the hash of the kernel's sources when the counters were taken; a
 # kernel edited since then reports traffic null.  See profiles/traffic_*.md.
 TRAFFIC = {
-    "conv": {"src": "7b780394d52d24f2", "fetch_bytes": 266688843, "write_bytes": 130641104},
-    "conv_bf16": {"src": "7b780394d52d24f2", "fetch_bytes": 136705458, "write_bytes": 80347680},
-    "maxpool": {"src": "628c5336c160dc49", "fetch_bytes": 2160260234, "write_bytes": 2140746016},
-    "maxpool_s2": {"src": "628c5336c160dc49", "fetch_bytes": 2176863633, "write_bytes": 536870912},
-    "maxpool_d2": {"src": "628c5336c160dc49", "fetch_bytes": 2266848453, "write_bytes": 2147483648},
-    "convT": {"src": "19452b55b8ce8c8c", "fetch_bytes": 141140378, "write_bytes": 1260160384},
-    "convT_bf16": {"src": "6e57bf9ac0b37673", "fetch_bytes": 77817876, "write_bytes": 772167728},
-    "conv_general": {"src": "456ad05d0ed2d488", "fetch_bytes": 137133028, "write_bytes": 69415152},
-    "conv_2stage#0": {"src": "8cfb246101a56548", "fetch_bytes": 277502105, "write_bytes": 2116773216},
-    "conv_2stage#1": {"src": "8cfb246101a56548", "fetch_bytes": 2104807670, "write_bytes": 152430560},
-    "convT_2stage#0": {"src": "3f02b739b4f13100", "fetch_bytes": 140682282, "write_bytes": 1296515872},
-    "convT_2stage#1": {"src": "3f02b739b4f13100", "fetch_bytes": 1223737195, "write_bytes": 1121207536},
+"conv": {"src": "7b780394d52d24f2", "fetch_bytes": 266689815, "write_bytes": 130639504},
+    "conv_bf16": {"src": "7b780394d52d24f2", "fetch_bytes": 136705825, "write_bytes": 80708896},
+    "maxpool": {"src": "628c5336c160dc49", "fetch_bytes": 2160266220, "write_bytes": 2140725392},
+    "maxpool_s2": {"src": "628c5336c160dc49", "fetch_bytes": 2176873823, "write_bytes": 536870912},
+    "maxpool_d2": {"src": "628c5336c160dc49", "fetch_bytes": 2266742728, "write_bytes": 2147483648},
+    "convT": {"src": "6537350baa635ead", "fetch_bytes": 141405260, "write_bytes": 1257970768},
+    "convT_bf16": {"src": "712a7c1de94f1105", "fetch_bytes": 77685289, "write_bytes": 773371792},
+    "conv_general": {"src": "456ad05d0ed2d488", "fetch_bytes": 137123860, "write_bytes": 69336304},
+    "conv_2stage#0": {"src": "8cfb246101a56548", "fetch_bytes": 277820215, "write_bytes": 2116929056},
+    "conv_2stage#1": {"src": "8cfb246101a56548", "fetch_bytes": 2104813379, "write_bytes": 152470528},
+    "convT_2stage#0": {"src": "19c24d078ac3a25f", "fetch_bytes": 140875997, "write_bytes": 1282924592},
+    "convT_2stage#1": {"src": "19c24d078ac3a25f", "fetch_bytes": 1223776700, "write_bytes": 1121257328},
 }
 KERNEL_SOURCES = {
     "conv": ["conv_pool.hip", "ps_internal.h"],
