@@ -88,7 +88,14 @@ def test_shape_query_errors(ps):
     assert lib.ps_conv2d_out_dim(10, 3, 1, -1, 1, ctypes.byref(out)) == ps.PS_ERR_PARAM
     assert lib.ps_conv2d_out_dim(2, 3, 1, 0, 1, ctypes.byref(out)) == ps.PS_ERR_SHAPE
     assert lib.ps_conv2d_out_dim(0, 1, 1, 0, 1, ctypes.byref(out)) == ps.PS_ERR_SHAPE
+    # extents past INT_MAX are rejected, not truncated (conv, and pool through it)
+    int_max = 2**31 - 1
+    assert lib.ps_conv2d_out_dim(int_max, 1, 1, 1, 1, ctypes.byref(out)) == ps.PS_ERR_SHAPE
+    assert lib.ps_pool2d_out_dim(int_max, 1, 1, 1, 1, ctypes.byref(out)) == ps.PS_ERR_SHAPE
+    assert lib.ps_convT2d_out_dim(int_max, 4, 2, 0, 0, 1, ctypes.byref(out)) == ps.PS_ERR_SHAPE
     assert out.value == -7  # untouched on error
+    assert lib.ps_conv2d_out_dim(int_max, 3, 1, 1, 1, ctypes.byref(out)) == ps.PS_OK
+    assert out.value == int_max
     # output_padding must be < max(stride, dilation)
     assert lib.ps_convT2d_out_dim(64, 4, 2, 1, 2, 1, ctypes.byref(out)) == ps.PS_ERR_PARAM
     assert lib.ps_convT2d_out_dim(64, 4, 2, 1, 1, 1, ctypes.byref(out)) == ps.PS_OK
