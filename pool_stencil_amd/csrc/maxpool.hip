@@ -427,6 +427,66 @@ __global__ __launch_bounds__(256) void maxpool_rows_sd(
     }
 }
 
+// Disjoint windows: stride = k (2 or 4), no padding or dilation, W even.  A thread
+// owns one output column of one output row; its window is k consecutive columns of k
+// consecutive rows, read as 8-byte vectors (8-byte aligned: k, W and the column
+// offset are even), so a wave's load of one window row is 64 contiguous 8k-byte
+// pieces and the k rows of an output row are one contiguous block of memory.  No
+// LDS and no lane exchange: a read-streaming kernel (the strided row-streaming
+// kernel stages rows through LDS and reads them back at stride k, which for these
+// windows made the epilogue + pool stage of the unfused conv pipeline run at 3.7 TB/s).
+// grid.x: 64-column chunks of the output row, grid.y: groups of 4 output rows (one
+// per wave), grid.z: planes (strided).  EPI as in maxpool_rows_sd.
+template <int K, bool EPI>
+__global__ __launch_bounds__(256) void maxpool_disjoint(const float *__restrict__ x,
+                                                        float *__restrict__ y, int H, int W,
+                                                        int OH, int OW, int planes,
+                                                        PoolEpi epi) {
+    static_assert(K % 2 == 0, "8-byte vectors");
+    const int ow = blockIdx.x * kWave + (threadIdx.x & (kWave - 1));
+    const int oh = blockIdx.y * 4 + (threadIdx.x >> 6);
+    if (ow >= OW || oh >= OH) return;
+    const float sgn = EPI ? epi.sgn : 1.f;
+    for (int pl = blockIdx.z; pl < planes; pl += gridDim.z) {
+        const float *xr = x + ((size_t)pl * H + (size_t)oh * K) * W + (size_t)ow * K;
+        float2 v[K][K / 2];
+#pragma unroll
+        for (int kh = 0; kh < K; ++kh)
+#pragma unroll
+            for (int h = 0; h < K / 2; ++h)
+                v[kh][h] = *(const float2 *)(xr + (size_t)kh * W + 2 * h);
+        // row-major order over the window, first maximum kept (as the other kernels)
+        float m = -INFINITY;
+#pragma unroll
+        for (int kh = 0; kh < K; ++kh)
+#pragma unroll
+            for (int h = 0; h < K / 2; ++h) {
+                m = fmax_ordered(m, sgn * v[kh][h].x);
+                m = fmax_ordered(m, sgn * v[kh][h].y);
+            }
+        if constexpr (EPI)
+            m = tanh_exp(sgn * m) * epi.scale + epi.b2[pl % epi.C];
+        y[((size_t)pl * OH + oh) * OW + ow] = m;
+    }
+}
+
+// stride = k in {2, 4}, d = 1, p = 0, W even; -1 otherwise
+template <bool EPI>
+int launch_disjoint(const float *x, float *y, int N, int C, int H, int W, int OH, int OW, int k,
+                    int s, int p, int d, const PoolEpi &epi, hipStream_t stream) {
+    if (s != k || d != 1 || p != 0 || (k != 2 && k != 4) || W % 2 != 0) return -1;
+    const int64_t planes = (int64_t)N * C;
+    if (planes > 0x7fffffff) return -1;
+    const dim3 grid((unsigned)((OW + kWave - 1) / kWave), (unsigned)((OH + 3) / 4),
+                    (unsigned)(planes < 65535 ? planes : 65535));
+    if (grid.y > 65535u) return -1;
+    if (k == 2)
+        return launch(maxpool_disjoint<2, EPI>, grid, dim3(256), 0, stream, x, y, H, W, OH, OW,
+                      (int)planes, epi);
+    return launch(maxpool_disjoint<4, EPI>, grid, dim3(256), 0, stream, x, y, H, W, OH, OW,
+                  (int)planes, epi);
+}
+
 int occupancy_cap_lds_bytes(int wgs, int static_bytes);
 
 template <int K, int S, int D, int V, bool EPI>
@@ -622,8 +682,9 @@ int launch_maxpool2d(const float *x, float *y, int N, int C, int H, int W, int O
         }
     }
     {
-        const int rc = launch_rows_sd_any<false>(x, y, N, C, H, W, OH, OW, k, s, p, d, PoolEpi{},
-                                                 stream);
+        int rc = launch_disjoint<false>(x, y, N, C, H, W, OH, OW, k, s, p, d, PoolEpi{}, stream);
+        if (rc >= 0) return rc;
+        rc = launch_rows_sd_any<false>(x, y, N, C, H, W, OH, OW, k, s, p, d, PoolEpi{}, stream);
         if (rc >= 0) return rc;
     }
     // output rows per thread: 8 at stride 1 (neighbouring rows share most input rows
@@ -661,6 +722,8 @@ int launch_tanh_scale_bias_maxpool_rows(const float *y, const float *bias2, floa
                                         int C, int H, int W, int OH, int OW, float scale, int k,
                                         int s, int p, int d, hipStream_t stream) {
     const PoolEpi epi{scale < 0.f ? -1.f : 1.f, scale, bias2, C};
+    const int rc = launch_disjoint<true>(y, out, N, C, H, W, OH, OW, k, s, p, d, epi, stream);
+    if (rc >= 0) return rc;
     return launch_rows_sd_any<true>(y, out, N, C, H, W, OH, OW, k, s, p, d, epi, stream);
 }
 

@@ -86,6 +86,10 @@ POOL_CASES = [
     (2, 1, 70, 70, 4, 3, 3, 1),     # k4 s3, the largest padding
     (1, 1, 200, 40, 5, 2, 4, 2),    # k5 s2 d2: 4 bands
     (3, 2, 66, 520, 2, 1, 1, 2),    # k2 s1 d2: 3 strips, a ragged last strip
+    # disjoint windows (stride = k in {2, 4}, no padding, even W): vector-load kernel
+    (2, 3, 37, 50, 4, 4, 0, 1),     # unused last row and columns
+    (1, 2, 130, 258, 2, 2, 0, 1),   # 3 column chunks, 17 row groups
+    (1, 1, 4, 2, 2, 2, 0, 1),       # one column
 ]
 
 

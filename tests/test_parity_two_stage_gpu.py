@@ -91,6 +91,10 @@ POOL_EPI_CASES = [
     (1, 2, 6, 6, 2, 1, 2, 1, 2.0),      # windows wholly in the padding -> -inf
     (1, 3, 150, 140, 4, 4, 1, 1, -0.6),  # row-streaming kernel: 5 bands, padding, scale < 0
     (1, 2, 70, 600, 3, 2, 1, 1, 1.3),   # 256-column strips, a ragged second strip
+    # disjoint windows, even W: the vector-load kernel (fp32)
+    (2, 5, 38, 42, 4, 4, 0, 1, -1.3),
+    (1, 3, 66, 130, 2, 2, 0, 1, 0.0),
+    (1, 64, 254, 254, 4, 4, 0, 1, 2.0),  # one image of the conv workload's stored output
 ]
 
 
