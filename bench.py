@@ -72,18 +72,18 @@ TINY_FLOP = 2 * 72 * 2 * 16 * 28 * 28              # the 28x28 conv outputs the 
 # x1.0.  `src` is the hash of the kernel's sources when the counters were taken; a
 # kernel edited since then reports traffic null.  See profiles/traffic_*.md.
 TRAFFIC = {
-"conv": {"src": "7b780394d52d24f2", "fetch_bytes": 266689815, "write_bytes": 130639504},
-    "conv_bf16": {"src": "7b780394d52d24f2", "fetch_bytes": 136705825, "write_bytes": 80708896},
-    "maxpool": {"src": "628c5336c160dc49", "fetch_bytes": 2160266220, "write_bytes": 2140725392},
-    "maxpool_s2": {"src": "628c5336c160dc49", "fetch_bytes": 2176873823, "write_bytes": 536870912},
-    "maxpool_d2": {"src": "628c5336c160dc49", "fetch_bytes": 2266742728, "write_bytes": 2147483648},
-    "convT": {"src": "6537350baa635ead", "fetch_bytes": 141405260, "write_bytes": 1257970768},
-    "convT_bf16": {"src": "712a7c1de94f1105", "fetch_bytes": 77685289, "write_bytes": 773371792},
-    "conv_general": {"src": "456ad05d0ed2d488", "fetch_bytes": 137123860, "write_bytes": 69336304},
-    "conv_2stage#0": {"src": "8cfb246101a56548", "fetch_bytes": 277820215, "write_bytes": 2116929056},
-    "conv_2stage#1": {"src": "8cfb246101a56548", "fetch_bytes": 2104813379, "write_bytes": 152470528},
-    "convT_2stage#0": {"src": "19c24d078ac3a25f", "fetch_bytes": 140875997, "write_bytes": 1282924592},
-    "convT_2stage#1": {"src": "19c24d078ac3a25f", "fetch_bytes": 1223776700, "write_bytes": 1121257328},
+    "conv": {"src": "7b780394d52d24f2", "fetch_bytes": 266689672, "write_bytes": 130660000},
+    "conv_bf16": {"src": "7b780394d52d24f2", "fetch_bytes": 136705816, "write_bytes": 80302576},
+    "maxpool": {"src": "7fe7bbddd12793d9", "fetch_bytes": 2160264997, "write_bytes": 2140695664},
+    "maxpool_s2": {"src": "7fe7bbddd12793d9", "fetch_bytes": 2176843024, "write_bytes": 536870912},
+    "maxpool_d2": {"src": "7fe7bbddd12793d9", "fetch_bytes": 2266587405, "write_bytes": 2147483648},
+    "convT": {"src": "6537350baa635ead", "fetch_bytes": 141395713, "write_bytes": 1255994896},
+    "convT_bf16": {"src": "712a7c1de94f1105", "fetch_bytes": 78111346, "write_bytes": 774150384},
+    "conv_general": {"src": "456ad05d0ed2d488", "fetch_bytes": 137128842, "write_bytes": 69310528},
+    "conv_2stage#0": {"src": "8cfb246101a56548", "fetch_bytes": 277656551, "write_bytes": 2116913712},
+    "conv_2stage#1": {"src": "8cfb246101a56548", "fetch_bytes": 2112061170, "write_bytes": 133779376},
+    "convT_2stage#0": {"src": "19c24d078ac3a25f", "fetch_bytes": 140857042, "write_bytes": 1281002192},
+    "convT_2stage#1": {"src": "19c24d078ac3a25f", "fetch_bytes": 1223691310, "write_bytes": 1121181168},
 }
 KERNEL_SOURCES = {
     "conv": ["conv_pool.hip", "ps_internal.h"],
