@@ -118,6 +118,20 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? PS_CONV_MIN_WAVES : 1)) void c
     const uint32_t sgn_bit = scale < 0.f ? 0x80000000u : 0u;
     float wr[4][9][CING];
     auto load_weights = [&](int ct) {
+        // Every weight of the tile present and scale >= 0 (a uniform test): plain loads,
+        // without the per-weight select and sign flip (144 VALU instructions per wave,
+        // which the matrix cores would wait for).
+        if (sgn_bit == 0u && Cin == CINP && ct + 64 <= Cout) {
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+                for (int g = 0; g < CING; ++g) {
+                    const float *wp = w + ((size_t)(ct + 16 * nt + j) * Cin + 4 * g + g4) * 9;
+#pragma unroll
+                    for (int tap = 0; tap < 9; ++tap) wr[nt][tap][g] = wp[tap];
+                }
+            return;
+        }
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
             const int co = ct + 16 * nt + j;
@@ -136,11 +150,17 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? PS_CONV_MIN_WAVES : 1)) void c
             }
         }
     };
+    // Epilogue constants: with u = sgn*best + cb, tanh(u) = 1 - 2/(2^(2u log2e) + 1), so
+    // out = (scale + b2) - 2 scale / (2^(best*k2 + cb*2log2e) + 1), k2 = 2 log2e sgn:
+    // s_bias holds cb*2log2e and scale + b2.
+    constexpr float kTwoLog2e = 2.8853900817779268f;
+    const float k2 = sgn * kTwoLog2e;
+    const float m2 = -2.f * scale;
     auto stage_bias = [&](int ct) {
         if (threadIdx.x < 64) {
             const int co = ct + threadIdx.x;
-            s_bias[0][threadIdx.x] = (co < Cout && cb) ? cb[co] : 0.f;
-            s_bias[1][threadIdx.x] = co < Cout ? b2[co] : 0.f;
+            s_bias[0][threadIdx.x] = (co < Cout && cb) ? cb[co] * kTwoLog2e : 0.f;
+            s_bias[1][threadIdx.x] = co < Cout ? scale + b2[co] : 0.f;
         }
     };
     // first tile's weights and biases: in flight together with the halo loads
@@ -366,9 +386,9 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? PS_CONV_MIN_WAVES : 1)) void c
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int cl = 16 * nt + 4 * g4 + r;
-                const float v = sgn * best[nt][r] + s_bias[0][cl];
+                const float e = __builtin_amdgcn_exp2f(fmaf(best[nt][r], k2, s_bias[0][cl]));
                 __builtin_amdgcn_raw_buffer_store_b32(
-                    __float_as_uint(tanh_exp(v) * scale + s_bias[1][cl]), yr,
+                    __float_as_uint(fmaf(m2, __builtin_amdgcn_rcpf(e + 1.f), s_bias[1][cl])), yr,
                     lane_off + 4u * (uint32_t)(ct + 16 * nt + r) * cplane, 0, 0);
             }
     }
