@@ -47,6 +47,7 @@ namespace ps {
 namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int pad_words_16mod64(int n) { return n + ((16 - (n % 64)) + 64) % 64; }
@@ -84,6 +85,9 @@ struct TileGeom {
 #endif
 #ifndef PS_BF16_LDS_AHEAD
 #define PS_BF16_LDS_AHEAD 3
+#endif
+#ifndef PS_BF16_W32_AHEAD
+#define PS_BF16_W32_AHEAD 3
 #endif
 #ifndef PS_CONV_MIN_WAVES
 #define PS_CONV_MIN_WAVES 3
@@ -402,7 +406,7 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? PS_CONV_MIN_WAVES : 1)) void c
 // rows that pooled row ph+1 adds are loaded from HBM during the MFMA work of row ph
 // (into an LDS staging area when rows are 16-byte aligned, else into registers) and
 // transposed into the ring afterwards.  One barrier per row.
-template <int PK, int NPW, bool VEC, bool MULTI>
+template <int PK, int NPW, bool VEC, bool MULTI, bool W32>
 __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? 2 : 1)) void conv_pool_bf16(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, const float *__restrict__ cb,
     const float *__restrict__ b2, uint16_t *__restrict__ y, int Cin, int H, int W, int Cout,
@@ -519,6 +523,35 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? 2 : 1)) void conv_pool_bf16(
             }
         }
     };
+    // W32 (v_mfma_f32_32x32x16_bf16, one 64-channel tile): wave wv owns channels
+    // 32*(wv & 1) .. +31 and pooled columns 32*(wv >> 1) .. +31 of the strip; lane l
+    // is pixel (B/D column) l & 31 and, as A row, channel 32*(wv & 1) + (l & 31).  K-step
+    // s (0..4) = kernel taps 2s, 2s+1 x 8 channels, lane half h = l >> 5 taking tap 2s + h
+    // (tap 9 carries zero weights): 80 K per window position instead of 96, and half
+    // as many matrix instructions, each twice as large, as the 16x16x32 form.
+    const int h32 = lane >> 5, n32 = lane & 31;
+    const int cw32 = wv & 1, px32 = wv >> 1;
+    bf16x8 wa32[W32 ? 5 : 1];
+    auto load_weights32 = [&]() {
+        const int co = 32 * cw32 + n32;
+#pragma unroll
+        for (int s = 0; s < (W32 ? 5 : 1); ++s) {
+            const int tap = 2 * s + h32;
+            uint32_t hv[8];
+#pragma unroll
+            for (int ci = 0; ci < 8; ++ci) {
+                const bool ok = co < Cout && ci < Cin && tap < 9;
+                const uint32_t v = w[ok ? ((size_t)co * Cin + ci) * 9 + tap : 0];
+                hv[ci] = ok ? v : 0u;
+            }
+            uint4 pk;
+            pk.x = (hv[0] | (hv[1] << 16)) ^ wsign;
+            pk.y = (hv[2] | (hv[3] << 16)) ^ wsign;
+            pk.z = (hv[4] | (hv[5] << 16)) ^ wsign;
+            pk.w = (hv[6] | (hv[7] << 16)) ^ wsign;
+            wa32[s] = __builtin_bit_cast(bf16x8, pk);
+        }
+    };
     // Epilogue constants: with u = sgn*best + cb, tanh(u) = 1 - 2/(2^(2u log2e) + 1), so
     // out = (scale + b2) - 2 scale / (2^(best*k2 + cb*2log2e) + 1), k2 = 2 log2e sgn.
     constexpr float kTwoLog2e = 2.8853900817779268f;
@@ -546,22 +579,25 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? 2 : 1)) void conv_pool_bf16(
         }
     }
 
-    // Per lane, K-step s covers kernel tap 4*s + g4 (taps >= 9 carry zero weights
-    // and read a valid in-ring entry).  Column part of the ring offset per (s, dx).
-    int coff[3][PK];
-    int khs[3];
+    // Per lane, K-step s covers kernel tap 4*s + g4 (W32: 2*s + h32); taps >= 9 carry
+    // zero weights and read a valid in-ring entry.  Column part of the ring offset per
+    // (s, dx), and the lane's pooled column within the strip.
+    constexpr int NS = W32 ? 5 : 3;
+    const int pwl = W32 ? 32 * px32 + n32 : 16 * wv + j;
+    int coff[NS][PK];
+    int khs[NS];
 #pragma unroll
-    for (int s = 0; s < 3; ++s) {
-        const int tap = min(4 * s + g4, 8);
+    for (int s = 0; s < NS; ++s) {
+        const int tap = min(W32 ? 2 * s + h32 : 4 * s + g4, 8);
         const int kh = tap / 3, kw = tap % 3;
         khs[s] = kh;
 #pragma unroll
         for (int dx = 0; dx < PK; ++dx) {
             const int t = dx + kw;
-            coff[s][dx] = (t % PK) * G::Q + 16 * wv + j + t / PK;
+            coff[s][dx] = (t % PK) * G::Q + pwl + t / PK;
         }
     }
-    const int pw = pwt * G::T + 16 * wv + j;
+    const int pw = pwt * G::T + pwl;
     const float k2 = scale < 0.f ? -kTwoLog2e : kTwoLog2e;
     const float m2 = -2.f * scale;
     // Output stores go through a range-checked resource over image n's Cout planes:
@@ -571,11 +607,16 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? 2 : 1)) void conv_pool_bf16(
     const uint32_t cplane = (uint32_t)(PH * PW);
     const __amdgpu_buffer_rsrc_t yr =
         make_range_checked(y + (size_t)n * Cout * cplane, 2u * (uint32_t)Cout * cplane);
-    const uint32_t lane_off = pw < PW ? 2u * ((uint32_t)(4 * g4) * cplane + (uint32_t)pw) : 0x80000000u;
+    // (the lane's first channel: 4*g4, W32 32*(wv & 1) + 4*h32)
+    const uint32_t lane_c0 = W32 ? 32 * cw32 + 4 * h32 : 4 * g4;
+    const uint32_t lane_off = pw < PW ? 2u * (lane_c0 * cplane + (uint32_t)pw) : 0x80000000u;
     // MULTI: Cout > 64, the weights and biases of each 64-channel tile are reloaded per row
     constexpr bool single_tile = !MULTI;
     if constexpr (single_tile) {
-        load_weights(0);
+        if constexpr (W32)
+            load_weights32();
+        else
+            load_weights(0);
         stage_bias(0);
     }
     __syncthreads();
@@ -608,6 +649,24 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? 2 : 1)) void conv_pool_bf16(
             }
         }
 
+        // write the prefetched rows of pooled row ph + 1 into the ring
+        auto refill = [&]() {
+#pragma unroll
+            for (int i = 0; i < NPER; ++i) {
+                const int e = threadIdx.x + i * NT;
+                if (e < NTOT) {
+                    if constexpr (VEC) {
+                        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's loads have landed
+                        uint4 v[8];
+#pragma unroll
+                        for (int ci = 0; ci < 8; ++ci) v[ci] = stage[i][wvu][ci][lane];
+                        store_group(nr0 + e / NG, e % NG, v);
+                    } else {
+                        store_group(nr0 + e / NG, e % NG, pre[i]);
+                    }
+                }
+            }
+        };
         const int rbase = PK * ph - pad;
         for (int ct = 0; ct < Cout; ct += 64) {
             if constexpr (!single_tile) {
@@ -622,17 +681,18 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? 2 : 1)) void conv_pool_bf16(
             // pool max of positions p-2 and p-1 (one v_max3 per value) is taken after
             // position p's first MFMAs, when their results are long complete.
             constexpr int NPOS = PK * PK;
-            constexpr int NFR = 3 * NPOS;
-            constexpr int AHEAD_REQ = (MULTI || !VEC) && PS_BF16_LDS_AHEAD > 2 ? 2 : PS_BF16_LDS_AHEAD;
+            constexpr int NFR = NS * NPOS;
+            constexpr int AHEAD_REQ = W32 ? PS_BF16_W32_AHEAD
+                                      : (MULTI || !VEC) && PS_BF16_LDS_AHEAD > 2 ? 2 : PS_BF16_LDS_AHEAD;
             constexpr int AHEAD = AHEAD_REQ < NFR ? AHEAD_REQ : NFR;
             // the variants with more live registers (row loads held in registers, or
             // several channel tiles) take the pool max at the first K-step
-            constexpr int MAX_STEP = (MULTI || !VEC) ? 0 : PS_BF16_MAX_STEP;
-            int ridx[3][PK];  // ring entry index of kernel row khs[s] for window row dy
+            constexpr int MAX_STEP = W32 ? 2 : (MULTI || !VEC) ? 0 : PS_BF16_MAX_STEP;
+            int ridx[NS][PK];  // ring entry index of kernel row khs[s] for window row dy
             {
                 const int rb = ((rbase % RING) + RING) % RING;
 #pragma unroll
-                for (int s = 0; s < 3; ++s)
+                for (int s = 0; s < NS; ++s)
 #pragma unroll
                     for (int dy = 0; dy < PK; ++dy) {
                         const int r = rb + dy + khs[s];
@@ -640,19 +700,69 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? 2 : 1)) void conv_pool_bf16(
                     }
             }
             auto frag = [&](int f) {
-                const int pp = f / 3, s = f % 3;
+                const int pp = f / NS, s = f % NS;
                 return __builtin_bit_cast(bf16x8, ring[ridx[s][pp / PK] + coff[s][pp % PK]]);
             };
+            bf16x8 bq[AHEAD];
+#pragma unroll
+            for (int f = 0; f < AHEAD; ++f) bq[f] = frag(f);
+            if constexpr (W32) {
+                // D (32x32): lane l, register r = channel 32*(wv & 1) + 8*(r/4) + 4*h32 + r%4
+                // of the tile, pooled column pwl.  Positions as above, five K-steps each.
+                f32x16 best;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) best[r] = -INFINITY;
+                f32x16 acc[3];
+#pragma unroll
+                for (int f = 0; f < NFR; ++f) {
+                    const int pp = f / NS, s = f % NS;
+                    const bf16x8 b = bq[f % AHEAD];
+                    if (f + AHEAD < NFR) bq[f % AHEAD] = frag(f + AHEAD);
+                    acc[pp % 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        wa32[s], b, s == 0 ? (f32x16){} : acc[pp % 3], 0, 0, 0);
+                    if (s == MAX_STEP && pp >= 2 && pp % 2 == 0) {
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            best[r] = fmaxf(fmaxf(best[r], acc[(pp - 2) % 3][r]), acc[(pp - 1) % 3][r]);
+                        asm volatile("" : "+v"(best));
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    if constexpr (NPOS % 2 == 0)
+                        best[r] = fmaxf(fmaxf(best[r], acc[(NPOS - 2) % 3][r]), acc[(NPOS - 1) % 3][r]);
+                    else
+                        best[r] = fmaxf(best[r], acc[(NPOS - 1) % 3][r]);
+                }
+                if (more) refill();
+                // output (n, co = 32*(wv & 1) + 8*(r/4) + 4*h32 + r%4, ph, pw)
+                const uint32_t row_off = lane_off + 2u * (uint32_t)(ph * PW);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int c0 = 32 * cw32 + 8 * q + 4 * h32;
+                    const float4 cbv = *(const float4 *)&s_bias[0][c0];
+                    const float4 c2v = *(const float4 *)&s_bias[1][c0];
+                    const float cbr[4] = {cbv.x, cbv.y, cbv.z, cbv.w};
+                    const float c2r[4] = {c2v.x, c2v.y, c2v.z, c2v.w};
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float e = __builtin_amdgcn_exp2f(fmaf(best[4 * q + r], k2, cbr[r]));
+                        const float o = fmaf(m2, __builtin_amdgcn_rcpf(e + 1.f), c2r[r]);
+                        __builtin_amdgcn_raw_buffer_store_b16(
+                            f32_to_bf16_rne(o), yr, (int)(row_off + 2u * (uint32_t)(8 * q + r) * cplane),
+                            0, 0);
+                    }
+                }
+                continue;
+            }
             f32x4 best[4];
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) best[nt] = (f32x4){-INFINITY, -INFINITY, -INFINITY, -INFINITY};
             f32x4 acc[3][4];
-            bf16x8 bq[AHEAD];
-#pragma unroll
-            for (int f = 0; f < AHEAD; ++f) bq[f] = frag(f);
 #pragma unroll
             for (int f = 0; f < NFR; ++f) {
-                const int pp = f / 3, s = f % 3;
+                const int pp = f / NS, s = f % NS;
                 const bf16x8 b = bq[f % AHEAD];
                 if (f + AHEAD < NFR) bq[f % AHEAD] = frag(f + AHEAD);
 #pragma unroll
@@ -689,23 +799,7 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? 2 : 1)) void conv_pool_bf16(
             // stores (their ring slots are not read by row ph), so that waiting for the
             // loads does not also wait for the output stores (on this chip a wait on a
             // load issued before pending stores waits for those stores too).
-            if (single_tile && more) {
-#pragma unroll
-                for (int i = 0; i < NPER; ++i) {
-                    const int e = threadIdx.x + i * NT;
-                    if (e < NTOT) {
-                        if constexpr (VEC) {
-                            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's loads have landed
-                            uint4 v[8];
-#pragma unroll
-                            for (int ci = 0; ci < 8; ++ci) v[ci] = stage[i][wvu][ci][lane];
-                            store_group(nr0 + e / NG, e % NG, v);
-                        } else {
-                            store_group(nr0 + e / NG, e % NG, pre[i]);
-                        }
-                    }
-                }
-            }
+            if (single_tile && more) refill();
             // output (n, co = ct + 16 nt + 4 g4 + r, ph, pw)
             const uint32_t row_off = lane_off + 2u * ((uint32_t)ct * cplane + (uint32_t)(ph * PW));
 #pragma unroll
@@ -724,23 +818,7 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? 2 : 1)) void conv_pool_bf16(
                 }
             }
         }
-        if (!single_tile && more) {
-#pragma unroll
-            for (int i = 0; i < NPER; ++i) {
-                const int e = threadIdx.x + i * NT;
-                if (e < NTOT) {
-                    if constexpr (VEC) {
-                        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's loads have landed
-                        uint4 v[8];
-#pragma unroll
-                        for (int ci = 0; ci < 8; ++ci) v[ci] = stage[i][wvu][ci][lane];
-                        store_group(nr0 + e / NG, e % NG, v);
-                    } else {
-                        store_group(nr0 + e / NG, e % NG, pre[i]);
-                    }
-                }
-            }
-        }
+        if (!single_tile && more) refill();
         __syncthreads();
     }
 }
@@ -766,14 +844,17 @@ int launch_pk_npw(const void *x, const void *w, const float *cb, const float *b2
         const bool vec = (pad % 8 == 0) && (W % 8 == 0);
         const bool multi = Cout > 64;
         const dim3 grid((unsigned)nblocks), block(64 * NPW);
-#define PS_BF16_LAUNCH(V, M)                                                                  \
-    launch(conv_pool_bf16<PK, NPW, V, M>, grid, block, 0, stream, (const uint16_t *)x,        \
+#define PS_BF16_LAUNCH(V, M, W32)                                                             \
+    launch(conv_pool_bf16<PK, NPW, V, M, W32>, grid, block, 0, stream, (const uint16_t *)x,   \
            (const uint16_t *)w, cb, b2, (uint16_t *)y, Cin, H, W, Cout, pad, PH, PW, scale,   \
            npwt, (int)nseg)
-        if (vec && !multi) return PS_BF16_LAUNCH(true, false);
-        if (vec) return PS_BF16_LAUNCH(true, true);
-        if (!multi) return PS_BF16_LAUNCH(false, false);
-        return PS_BF16_LAUNCH(false, true);
+        // one channel tile, pool <= 4, 32 or 64 columns per strip and rows staged through
+        // LDS: the 32x32x16 form (with rows held in registers it would spill)
+        constexpr bool w32 = PK <= 4 && (NPW == 2 || NPW == 4);
+        if (vec && !multi) return PS_BF16_LAUNCH(true, false, w32);
+        if (vec) return PS_BF16_LAUNCH(true, true, false);
+        if (!multi) return PS_BF16_LAUNCH(false, false, false);
+        return PS_BF16_LAUNCH(false, true, false);
 #undef PS_BF16_LAUNCH
     }
     const uint64_t nblocks = (uint64_t)N * PH * npwt;

@@ -220,6 +220,13 @@ CONV_CASES = [
     dict(N=128, Cin=8, H=34, W=96, Cout=130, pool_k=4, pool_stride=4),  # 3 channel tiles
     dict(N=64, Cin=8, H=30, W=64, Cout=96, pool_k=2, pool_stride=2),    # 2 channel tiles
     dict(N=128, Cin=8, H=64, W=128, Cout=16, pool_k=7, pool_stride=7),  # 2 groups
+    # 16-byte rows, pool <= 4, one channel tile, 32 or 64 columns per strip: the bf16
+    # kernel's 32x32x16 form (channel halves and column halves per wave), with ragged
+    # channels and columns, Cin < 8, a window minimum, no conv bias and scale 0
+    dict(N=16, Cin=5, H=36, W=128, Cout=40, pool_k=4, pool_stride=4),   # 31 columns
+    dict(N=8, Cin=8, H=38, W=216, Cout=64, pool_k=4, pool_stride=4, scale=-0.7),  # 53
+    dict(N=8, Cin=8, H=26, W=136, Cout=48, pool_k=3, pool_stride=3, conv_bias=False),
+    dict(N=32, Cin=8, H=34, W=72, Cout=16, pool_k=2, pool_stride=2, scale=0.0),   # 35
 ]
 
 
