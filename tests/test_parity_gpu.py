@@ -86,6 +86,17 @@ POOL_CASES = [
     (2, 1, 70, 70, 4, 3, 3, 1),     # k4 s3, the largest padding
     (1, 1, 200, 40, 5, 2, 4, 2),    # k5 s2 d2: 4 bands
     (3, 2, 66, 520, 2, 1, 1, 2),    # k2 s1 d2: 3 strips, a ragged last strip
+    # stride-1 row kernel, k <= 4 with every padding below k, rows of 260..1020
+    # columns (one and two strips), several bands
+    (1, 3, 100, 260, 2, 1, 0, 1),
+    (2, 2, 70, 264, 2, 1, 1, 1),
+    (1, 2, 66, 300, 3, 1, 0, 1),
+    (1, 2, 66, 516, 3, 1, 1, 1),    # 1 KB rows
+    (1, 1, 40, 1020, 3, 1, 2, 1),
+    (2, 1, 70, 400, 4, 1, 0, 1),
+    (1, 2, 35, 388, 4, 1, 2, 1),
+    (1, 1, 96, 1016, 4, 1, 3, 1),
+    (1, 5, 100, 512, 4, 1, 1, 1),   # 4 bands a plane: planes straddle workgroups
     # disjoint windows (stride = k in {2, 4}, no padding, even W): vector-load kernel
     (2, 3, 37, 50, 4, 4, 0, 1),     # unused last row and columns
     (1, 2, 130, 258, 2, 2, 0, 1),   # 3 column chunks, 17 row groups
