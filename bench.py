@@ -72,18 +72,18 @@ TINY_FLOP = 2 * 72 * 2 * 16 * 28 * 28              # the 28x28 conv outputs the 
 # x1.0.  `src` is the hash of the kernel's sources when the counters were taken; a
 # kernel edited since then reports traffic null.  See profiles/traffic_*.md.
 TRAFFIC = {
-    "conv": {"src": "7b780394d52d24f2", "fetch_bytes": 266689672, "write_bytes": 130660000},
-    "conv_bf16": {"src": "7b780394d52d24f2", "fetch_bytes": 136705816, "write_bytes": 80302576},
-    "maxpool": {"src": "7fe7bbddd12793d9", "fetch_bytes": 2160264997, "write_bytes": 2140695664},
-    "maxpool_s2": {"src": "7fe7bbddd12793d9", "fetch_bytes": 2176843024, "write_bytes": 536870912},
-    "maxpool_d2": {"src": "7fe7bbddd12793d9", "fetch_bytes": 2266587405, "write_bytes": 2147483648},
-    "convT": {"src": "6537350baa635ead", "fetch_bytes": 141395713, "write_bytes": 1255994896},
-    "convT_bf16": {"src": "712a7c1de94f1105", "fetch_bytes": 78111346, "write_bytes": 774150384},
-    "conv_general": {"src": "456ad05d0ed2d488", "fetch_bytes": 137128842, "write_bytes": 69310528},
-    "conv_2stage#0": {"src": "8cfb246101a56548", "fetch_bytes": 277656551, "write_bytes": 2116913712},
-    "conv_2stage#1": {"src": "8cfb246101a56548", "fetch_bytes": 2112061170, "write_bytes": 133779376},
-    "convT_2stage#0": {"src": "19c24d078ac3a25f", "fetch_bytes": 140857042, "write_bytes": 1281002192},
-    "convT_2stage#1": {"src": "19c24d078ac3a25f", "fetch_bytes": 1223691310, "write_bytes": 1121181168},
+    "conv": {"src": "fe174b0a4b5fe422", "fetch_bytes": 266679880, "write_bytes": 130646080},
+    "conv_bf16": {"src": "fe174b0a4b5fe422", "fetch_bytes": 136599226, "write_bytes": 80936496},
+    "maxpool": {"src": "7fe7bbddd12793d9", "fetch_bytes": 2160264738, "write_bytes": 2140656144},
+    "maxpool_s2": {"src": "7fe7bbddd12793d9", "fetch_bytes": 2176851465, "write_bytes": 536870912},
+    "maxpool_d2": {"src": "7fe7bbddd12793d9", "fetch_bytes": 2266669678, "write_bytes": 2147483648},
+    "convT": {"src": "6537350baa635ead", "fetch_bytes": 141521563, "write_bytes": 1257740000},
+    "convT_bf16": {"src": "712a7c1de94f1105", "fetch_bytes": 77301498, "write_bytes": 774169744},
+    "conv_general": {"src": "456ad05d0ed2d488", "fetch_bytes": 137143017, "write_bytes": 69383008},
+    "conv_2stage#0": {"src": "8cfb246101a56548", "fetch_bytes": 277549417, "write_bytes": 2117104448},
+    "conv_2stage#1": {"src": "8cfb246101a56548", "fetch_bytes": 2112060730, "write_bytes": 133774768},
+    "convT_2stage#0": {"src": "19c24d078ac3a25f", "fetch_bytes": 141098281, "write_bytes": 1281986480},
+    "convT_2stage#1": {"src": "19c24d078ac3a25f", "fetch_bytes": 1223835078, "write_bytes": 1121307664},
 }
 KERNEL_SOURCES = {
     "conv": ["conv_pool.hip", "ps_internal.h"],
