@@ -33,10 +33,11 @@
 //
 // fp32: v_mfma_f32_16x16x4_f32 (fp32 products and accumulation), one K-step
 //       = one kernel tap x 4 input channels.
-// bf16: v_mfma_f32_16x16x32_bf16 (exact bf16 products, fp32 accumulation), one
-//       K-step = 4 kernel taps x 8 input channels; the LDS tile is channel-last
-//       so one 16-byte LDS read gives a lane its 8 channels.  Output rounded to
-//       nearest even.
+// bf16: exact bf16 products, fp32 accumulation; the LDS tile is channel-last so
+//       one 16-byte LDS read gives a lane its 8 channels.  One channel tile with
+//       pool <= 4: v_mfma_f32_32x32x16_bf16, one K-step = 2 kernel taps x 8 input
+//       channels (9 taps in 5 steps); otherwise v_mfma_f32_16x16x32_bf16, one K-step
+//       = 4 taps x 8 channels (9 taps in 3 steps).  Output rounded to nearest even.
 #include "ps_internal.h"
 
 #include <math.h>
@@ -86,6 +87,7 @@ struct TileGeom {
 #ifndef PS_BF16_LDS_AHEAD
 #define PS_BF16_LDS_AHEAD 3
 #endif
+// B fragments read ahead of their MFMAs in the 32x32x16 form (5 and 8 measured no faster)
 #ifndef PS_BF16_W32_AHEAD
 #define PS_BF16_W32_AHEAD 3
 #endif
