@@ -72,18 +72,18 @@ TINY_FLOP = 2 * 72 * 2 * 16 * 28 * 28              # the 28x28 conv outputs the 
 # x1.0.  `src` is the hash of the kernel's sources when the counters were taken; a
 # kernel edited since then reports traffic null.  See profiles/traffic_*.md.
 TRAFFIC = {
-    "conv": {"src": "fe174b0a4b5fe422", "fetch_bytes": 266679880, "write_bytes": 130646080},
-    "conv_bf16": {"src": "fe174b0a4b5fe422", "fetch_bytes": 136599226, "write_bytes": 80936496},
-    "maxpool": {"src": "7fe7bbddd12793d9", "fetch_bytes": 2160264738, "write_bytes": 2140656144},
-    "maxpool_s2": {"src": "7fe7bbddd12793d9", "fetch_bytes": 2176851465, "write_bytes": 536870912},
-    "maxpool_d2": {"src": "7fe7bbddd12793d9", "fetch_bytes": 2266669678, "write_bytes": 2147483648},
-    "convT": {"src": "6537350baa635ead", "fetch_bytes": 141521563, "write_bytes": 1257740000},
-    "convT_bf16": {"src": "712a7c1de94f1105", "fetch_bytes": 77301498, "write_bytes": 774169744},
-    "conv_general": {"src": "456ad05d0ed2d488", "fetch_bytes": 137143017, "write_bytes": 69383008},
-    "conv_2stage#0": {"src": "8cfb246101a56548", "fetch_bytes": 277549417, "write_bytes": 2117104448},
-    "conv_2stage#1": {"src": "8cfb246101a56548", "fetch_bytes": 2112060730, "write_bytes": 133774768},
-    "convT_2stage#0": {"src": "19c24d078ac3a25f", "fetch_bytes": 141098281, "write_bytes": 1281986480},
-    "convT_2stage#1": {"src": "19c24d078ac3a25f", "fetch_bytes": 1223835078, "write_bytes": 1121307664},
+    "conv": {"src": "3a907b7630850971", "fetch_bytes": 266679785, "write_bytes": 130648400},
+    "conv_bf16": {"src": "3a907b7630850971", "fetch_bytes": 136599178, "write_bytes": 81249680},
+    "maxpool": {"src": "7fe7bbddd12793d9", "fetch_bytes": 2160263517, "write_bytes": 2140745776},
+    "maxpool_s2": {"src": "7fe7bbddd12793d9", "fetch_bytes": 2176831551, "write_bytes": 536870912},
+    "maxpool_d2": {"src": "7fe7bbddd12793d9", "fetch_bytes": 2266584902, "write_bytes": 2147483648},
+    "convT": {"src": "6537350baa635ead", "fetch_bytes": 141447467, "write_bytes": 1256833888},
+    "convT_bf16": {"src": "712a7c1de94f1105", "fetch_bytes": 77619476, "write_bytes": 773675600},
+    "conv_general": {"src": "456ad05d0ed2d488", "fetch_bytes": 137132536, "write_bytes": 69362256},
+    "conv_2stage#0": {"src": "8cfb246101a56548", "fetch_bytes": 277926457, "write_bytes": 2116814672},
+    "conv_2stage#1": {"src": "8cfb246101a56548", "fetch_bytes": 2112059975, "write_bytes": 133777088},
+    "convT_2stage#0": {"src": "19c24d078ac3a25f", "fetch_bytes": 140768833, "write_bytes": 1282602000},
+    "convT_2stage#1": {"src": "19c24d078ac3a25f", "fetch_bytes": 1223686229, "write_bytes": 1121160960},
 }
 KERNEL_SOURCES = {
     "conv": ["conv_pool.hip", "ps_internal.h"],
