@@ -154,12 +154,12 @@ int ps_maxpool2d(const float *x, float *y, int N, int C, int H, int W, int k, in
  * x [N,Cin,H,W] float32, w [Cin,Cout,k,k] float32, convT_bias [Cout] float32 or NULL,
  * bias2 [Cout] float32, y [N,Cout,OH,OW] float32.
  * Supported: k = 4, stride = 2, dil = 1, any pad >= 0 with OH, OW >= 1,
- * output_padding in {0, 1}, Cout a multiple of 16 with 16 <= Cout <= 256, and
- * 1 <= Cin <= 256 where one parity class's fp32 weights stay resident in the LDS
- * of a compute unit: (Cout*(16*Cq + 4) + 2*Cout)*4 <= 160 KB with Cq = ceil(Cin/4)
- * (Cin <= 76 at Cout = 128, <= 68 at 144, <= 36 at 256); x with its channels
- * rounded up to 4*Cq, and y, below 2^29 elements each.  Beyond these
- * PS_ERR_UNSUPPORTED. */
+ * output_padding in {0, 1}, 1 <= Cout <= 256, and 1 <= Cin <= 256 where one parity
+ * class's fp32 weights stay resident in the LDS of a compute unit:
+ * (Cp*(16*Cq + 4) + 2*Cp)*4 <= 160 KB with Cp = Cout rounded up to a multiple of 16
+ * and Cq = ceil(Cin/4) (Cin <= 76 at Cp = 128, <= 68 at 144, <= 36 at 256); x with
+ * its channels rounded up to 4*Cq, and y with Cp channels, below 2^29 elements each.
+ * Beyond these PS_ERR_UNSUPPORTED. */
 int ps_convT_softmax_bias_scale_sigmoid(
     const float *x, const float *w, const float *convT_bias, const float *bias2, float *y,
     int N, int Cin, int H, int W, int Cout, int k, int stride, int pad, int output_padding,

@@ -171,7 +171,7 @@ int ps_convT_softmax_bias_scale_sigmoid(const float *x, const float *w, const fl
     if (too_big(N, Cin, H, W) || too_big(N, Cout, OH, OW) || too_big(Cin, Cout, k, k))
         return PS_ERR_SHAPE;
     if (k != 4 || stride != 2 || dil != 1) return PS_ERR_UNSUPPORTED;
-    if (Cout % 16 != 0 || Cout > 256 || Cin > 256) return PS_ERR_UNSUPPORTED;
+    if (Cout > 256 || Cin > 256) return PS_ERR_UNSUPPORTED;
     if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return PS_ERR_ALIGN;
     return ps::launch_convT_softmax(x, w, convT_bias, bias2, y, N, Cin, H, W, Cout, OH, OW, pad,
                                     scale, (hipStream_t)stream);
@@ -216,7 +216,7 @@ int ps_convT2d(const float *x, const float *w, const float *bias, float *y, int 
     if (too_big(N, Cin, H, W) || too_big(N, Cout, OH, OW) || too_big(Cin, Cout, k, k))
         return PS_ERR_SHAPE;
     if (k != 4 || stride != 2 || dil != 1) return PS_ERR_UNSUPPORTED;
-    if (Cout % 16 != 0 || Cout > 256 || Cin > 256) return PS_ERR_UNSUPPORTED;
+    if (Cout > 256 || Cin > 256) return PS_ERR_UNSUPPORTED;
     if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return PS_ERR_ALIGN;
     return ps::launch_convT(x, w, bias, y, N, Cin, H, W, Cout, OH, OW, pad, (hipStream_t)stream);
 }

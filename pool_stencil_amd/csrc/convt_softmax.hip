@@ -69,7 +69,10 @@ template <int MT, int NQ, bool SOFTMAX>
 __global__ __launch_bounds__(kThreads) void convT_softmax_f32(
     const float *__restrict__ x, const float *__restrict__ w, const float *__restrict__ cbias,
     const float *__restrict__ b2, float *__restrict__ y, int N, int Cin, int H, int W, int OH,
-    int OW, int pad, float scale, int Cq, ClassGeom geo) {
+    int OW, int pad, float scale, int Cq, int Cout, ClassGeom geo) {
+    // Cout output channels padded to COUT = 16*MT: the padded channels get zero weights,
+    // a convT bias of -inf with the softmax (so they add nothing to the channel max and
+    // sum) and no stores
     constexpr int COUT = 16 * MT;
     extern __shared__ float lds[];
     const int KS = 4 * Cq;          // K-steps per lane group
@@ -92,7 +95,7 @@ __global__ __launch_bounds__(kThreads) void convT_softmax_f32(
     const int kb = (b + pad) & 1, rb = (b + pad) >> 1;
 
     // ---- stage A_ab: lw[co][G][s] = w[ci][co][ka+2u][kb+2v],
-    //      ci = G*Cq + s/4, (u, v) = ((s%4)/2, (s%4)%2); zero for ci >= Cin
+    //      ci = G*Cq + s/4, (u, v) = ((s%4)/2, (s%4)%2); zero for ci >= Cin or co >= Cout
     for (int e = threadIdx.x; e < COUT * 4 * KS; e += kThreads) {
         const int s = e % KS;
         const int G = (e / KS) & 3;
@@ -101,13 +104,18 @@ __global__ __launch_bounds__(kThreads) void convT_softmax_f32(
         const int u = (s >> 1) & 1, v = s & 1;
         const int kh = ka + 2 * u, kw = kb + 2 * v;
         float val = 0.f;
-        if (ci < Cin) val = w[(((size_t)ci * COUT + co) * 4 + kh) * 4 + kw];
+        if (ci < Cin && co < Cout) val = w[(((size_t)ci * Cout + co) * 4 + kh) * 4 + kw];
         lw[co * CS + G * KS + s] = val;
     }
     for (int e = threadIdx.x; e < COUT; e += kThreads) {
-        const float cb = cbias ? cbias[e] : 0.f;
-        lcb[e] = SOFTMAX ? cb * kLog2e : cb;
-        if constexpr (SOFTMAX) lb2[e] = -b2[e] * scale * kLog2e;  // b2 is NULL without it
+        if (e < Cout) {
+            const float cb = cbias ? cbias[e] : 0.f;
+            lcb[e] = SOFTMAX ? cb * kLog2e : cb;
+            if constexpr (SOFTMAX) lb2[e] = -b2[e] * scale * kLog2e;  // b2 is NULL without it
+        } else {
+            lcb[e] = SOFTMAX ? -INFINITY : 0.f;
+            if constexpr (SOFTMAX) lb2[e] = 0.f;
+        }
     }
     __syncthreads();
 
@@ -124,7 +132,9 @@ __global__ __launch_bounds__(kThreads) void convT_softmax_f32(
     const uint32_t plane = (uint32_t)H * W;
     const uint32_t xbytes = 4u * (uint32_t)N * Cin * plane;   // < 2^31 (host check)
     const uint32_t oplane = (uint32_t)OH * OW;
-    const uint32_t ybytes = 4u * (uint32_t)N * COUT * oplane;  // < 2^31 (host check)
+    const uint32_t ybytes = 4u * (uint32_t)N * Cout * oplane;  // < 2^31 (host check)
+    // channels 16*mt + 4G + r of the last channel tile at or past Cout are not stored
+    const int ylim = Cout - 16 * (MT - 1) - 4 * G;
     const __amdgpu_buffer_rsrc_t yr = make_range_checked(y, ybytes);
 
     // Waves wv and wv + 4 share a SIMD and have the same work per tile; started
@@ -157,7 +167,7 @@ __global__ __launch_bounds__(kThreads) void convT_softmax_f32(
             xo[nq][1] = r0 && c1 ? o - 4u : kMasked;
             xo[nq][2] = r1 && c0 ? o - 4u * W : kMasked;
             xo[nq][3] = r1 && c1 ? o - 4u * (W + 1) : kMasked;
-            yo[nq] = pok ? 4u * ((n * COUT + 4 * G) * oplane + (2 * m + a) * OW + (2 * q + b))
+            yo[nq] = pok ? 4u * ((n * Cout + 4 * G) * oplane + (2 * m + a) * OW + (2 * q + b))
                          : kMasked;
         }
 
@@ -257,7 +267,8 @@ __global__ __launch_bounds__(kThreads) void convT_softmax_f32(
 #pragma unroll
                     for (int nq = 0; nq < NQ; ++nq)
                         __builtin_amdgcn_raw_buffer_store_b32(
-                            __float_as_uint(acc[mt][nq][r] + cbv[r]), yr, yo[nq],
+                            __float_as_uint(acc[mt][nq][r] + cbv[r]), yr,
+                            mt < MT - 1 || r < ylim ? yo[nq] : kMasked,
                             (int)(4u * (uint32_t)(16 * mt + r) * oplane), 0);
             }
             continue;
@@ -304,7 +315,8 @@ __global__ __launch_bounds__(kThreads) void convT_softmax_f32(
                 for (int nq = 0; nq < NQ; ++nq) {
                     const float t = __builtin_amdgcn_exp2f(fmaf(acc[mt][nq][r], inv[nq], bv[r]));
                     __builtin_amdgcn_raw_buffer_store_b32(
-                        __float_as_uint(__builtin_amdgcn_rcpf(1.f + t)), yr, yo[nq],
+                        __float_as_uint(__builtin_amdgcn_rcpf(1.f + t)), yr,
+                        mt < MT - 1 || r < ylim ? yo[nq] : kMasked,
                         (int)(4u * (uint32_t)(16 * mt + r) * oplane), 0);
                 }
         }
@@ -313,7 +325,8 @@ __global__ __launch_bounds__(kThreads) void convT_softmax_f32(
 
 template <int MT, bool SOFTMAX>
 int launch_mt(const float *x, const float *w, const float *cb, const float *b2, float *y, int N,
-              int Cin, int H, int W, int OH, int OW, int pad, float scale, hipStream_t stream) {
+              int Cin, int H, int W, int Cout, int OH, int OW, int pad, float scale,
+              hipStream_t stream) {
     // pixel groups per wave tile: two (32 pixels) up to 128 channels; one beyond, so
     // that accumulators (4*MT*NQ) and A operands (4*MT) stay within the registers of
     // two waves per SIMD
@@ -381,7 +394,7 @@ int launch_mt(const float *x, const float *w, const float *cb, const float *b2, 
             hipSuccess)
         return PS_ERR_HIP;
     return launch(convT_softmax_f32<MT, NQ, SOFTMAX>, dim3(nblocks), dim3(kThreads), lds_bytes,
-                  stream, x, w, cb, b2, y, N, Cin, H, W, OH, OW, pad, scale, Cq, geo);
+                  stream, x, w, cb, b2, y, N, Cin, H, W, OH, OW, pad, scale, Cq, Cout, geo);
 }
 
 template <bool SOFTMAX>
@@ -389,8 +402,11 @@ int launch_cout(const float *x, const float *w, const float *cb, const float *b2
                 int Cin, int H, int W, int Cout, int OH, int OW, int pad, float scale,
                 hipStream_t stream) {
 #define PS_CONVT_MT(M) \
-    case M: return launch_mt<M, SOFTMAX>(x, w, cb, b2, y, N, Cin, H, W, OH, OW, pad, scale, stream)
-    switch (Cout / 16) {
+    case M:                                                                                  \
+        return launch_mt<M, SOFTMAX>(x, w, cb, b2, y, N, Cin, H, W, Cout, OH, OW, pad, scale,  \
+                                     stream)
+    // Cout rounded up to 16-channel tiles (the last one masked)
+    switch ((Cout + 15) / 16) {
         PS_CONVT_MT(1); PS_CONVT_MT(2); PS_CONVT_MT(3); PS_CONVT_MT(4);
         PS_CONVT_MT(5); PS_CONVT_MT(6); PS_CONVT_MT(7); PS_CONVT_MT(8);
         PS_CONVT_MT(9); PS_CONVT_MT(10); PS_CONVT_MT(11); PS_CONVT_MT(12);

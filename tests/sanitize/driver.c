@@ -137,7 +137,8 @@ static void entry_points(void) {
     EXPECT(ps_convT_softmax_bias_scale_sigmoid(fA, fA, NULL, NULL, fy, 2, 64, 8, 8, 128, 4, 2, 1, 1, 1, 2.f, NULL), PS_ERR_NULL);
     EXPECT(ps_convT_softmax_bias_scale_sigmoid(fA, fA, NULL, fA, fy, 2, 64, 8, 8, 128, 3, 2, 1, 1, 1, 2.f, NULL), PS_ERR_UNSUPPORTED);
     EXPECT(ps_convT_softmax_bias_scale_sigmoid(fA, fA, NULL, fA, fy, 2, 64, 8, 8, 128, 4, 2, 1, 2, 1, 2.f, NULL), PS_ERR_PARAM);
-    EXPECT(ps_convT_softmax_bias_scale_sigmoid(fA, fA, NULL, fA, fy, 2, 64, 8, 8, 120, 4, 2, 1, 1, 1, 2.f, NULL), PS_ERR_UNSUPPORTED);
+    EXPECT(ps_convT_softmax_bias_scale_sigmoid(fA, fA, NULL, fA, fy, 2, 64, 8, 8, 272, 4, 2, 1, 1, 1, 2.f, NULL), PS_ERR_UNSUPPORTED);
+    EXPECT(ps_convT_softmax_bias_scale_sigmoid(fA, fA, NULL, fA, fy, 2, 64, 8, 8, 120, 4, 2, 1, 1, 1, 2.f, NULL), 77);
     EXPECT(ps_convT_softmax_bias_scale_sigmoid(fA, fA, NULL, fA, fy, 2, 64, 8, 8, 128, 4, 2, 1, 1, 1, 2.f, NULL), 77);
     EXPECT(ps_convT_softmax_bias_scale_sigmoid(fA, fA, NULL, fA, fy, 1, 4, 3, 3, 16, 4, 2, 3, 0, 1, 2.f, NULL), 77);
     EXPECT(ps_convT_softmax_bias_scale_sigmoid_bf16(A, A, NULL, fA, A, 2, 64, 8, 8, 128, 4, 2, 1, 1, 1, 2.f, NULL), 77);
@@ -150,7 +151,7 @@ static void entry_points(void) {
     EXPECT(ps_softmax_bias_scale_sigmoid(fA, fA, fy, 2, 128, 9, 9, 2.f, NULL), 77);
     EXPECT(ps_softmax_bias_scale_sigmoid(fA, NULL, fy, 2, 128, 9, 9, 2.f, NULL), PS_ERR_NULL);
 #undef EXPECT
-    CHECK(ps_stub_calls - calls == 11, "accepted calls reaching a launcher: %d", ps_stub_calls - calls);
+    CHECK(ps_stub_calls - calls == 12, "accepted calls reaching a launcher: %d", ps_stub_calls - calls);
     for (int st = -1; st <= 8; ++st) CHECK(ps_status_string(st) != NULL, "status string %d", st);
 }
 

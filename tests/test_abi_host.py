@@ -189,7 +189,6 @@ def test_convT_validation(ps):
     assert _convT(lib, op=2) == ps.PS_ERR_PARAM
     assert _convT(lib, k=3) == ps.PS_ERR_UNSUPPORTED
     assert _convT(lib, s=3) == ps.PS_ERR_UNSUPPORTED
-    assert _convT(lib, Cout=24) == ps.PS_ERR_UNSUPPORTED
     assert _convT(lib, Cout=272) == ps.PS_ERR_UNSUPPORTED
     assert _convT(lib, Cin=80) == ps.PS_ERR_UNSUPPORTED     # a class's weights exceed the LDS
     assert _convT(lib, Cout=160) == ps.PS_ERR_UNSUPPORTED   # likewise at Cin = 64
@@ -211,7 +210,7 @@ def test_convT2d_validation(ps):
     assert call(H=0) == ps.PS_ERR_SHAPE
     assert call(op=2) == ps.PS_ERR_PARAM
     assert call(k=3) == ps.PS_ERR_UNSUPPORTED
-    assert call(Cout=40) == ps.PS_ERR_UNSUPPORTED
+    assert call(Cout=257) == ps.PS_ERR_UNSUPPORTED
     assert call(x=MISALIGNED) == ps.PS_ERR_ALIGN
 
 

@@ -319,6 +319,12 @@ CONVT_CASES = [
     dict(N=1, Cin=36, H=6, W=10, Cout=256),                   # the largest weight tile
     dict(N=1, Cin=20, H=5, W=7, Cout=240, pad=2, scale=-0.7),
     dict(N=3, Cin=9, H=4, W=6, Cout=176, pad=0, convT_bias=False),
+    # Cout not a multiple of 16: the last channel tile masked out of the softmax and
+    # the stores
+    dict(N=2, Cin=16, H=7, W=9, Cout=100),
+    dict(N=1, Cin=8, H=5, W=6, Cout=1),                       # softmax of one channel
+    dict(N=1, Cin=20, H=6, W=7, Cout=250, pad=0),
+    dict(N=3, Cin=9, H=4, W=5, Cout=37, scale=-0.8, convT_bias=False),
 ]
 
 

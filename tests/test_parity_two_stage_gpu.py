@@ -58,6 +58,8 @@ CONVT2D_CASES = [
     dict(N=1, Cin=16, H=6, W=9, Cout=64, pad=0),
     dict(N=1, Cin=12, H=7, W=6, Cout=48, pad=3, output_padding=0),
     dict(N=1, Cin=32, H=5, W=6, Cout=256),
+    dict(N=2, Cin=12, H=6, W=5, Cout=37),                     # Cout not a multiple of 16
+    dict(N=1, Cin=4, H=3, W=4, Cout=3, pad=0, output_padding=0),
     # the row-class kernel without its softmax epilogue
     dict(N=2, Cin=64, H=5, W=64, Cout=128),
     dict(N=1, Cin=24, H=6, W=72, Cout=128, pad=2, output_padding=0, convT_bias=False),
