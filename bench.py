@@ -72,18 +72,18 @@ TINY_FLOP = 2 * 72 * 2 * 16 * 28 * 28              # the 28x28 conv outputs the 
 # x1.0.  `src` is the hash of the kernel's sources when the counters were taken; a
 # kernel edited since then reports traffic null.  See profiles/traffic_*.md.
 TRAFFIC = {
-    "conv": {"src": "3a907b7630850971", "fetch_bytes": 266679785, "write_bytes": 130648400},
-    "conv_bf16": {"src": "3a907b7630850971", "fetch_bytes": 136599178, "write_bytes": 81249680},
-    "maxpool": {"src": "7fe7bbddd12793d9", "fetch_bytes": 2160263517, "write_bytes": 2140745776},
-    "maxpool_s2": {"src": "7fe7bbddd12793d9", "fetch_bytes": 2176831551, "write_bytes": 536870912},
-    "maxpool_d2": {"src": "7fe7bbddd12793d9", "fetch_bytes": 2266584902, "write_bytes": 2147483648},
-    "convT": {"src": "6537350baa635ead", "fetch_bytes": 141447467, "write_bytes": 1256833888},
-    "convT_bf16": {"src": "712a7c1de94f1105", "fetch_bytes": 77619476, "write_bytes": 773675600},
-    "conv_general": {"src": "456ad05d0ed2d488", "fetch_bytes": 137132536, "write_bytes": 69362256},
-    "conv_2stage#0": {"src": "8cfb246101a56548", "fetch_bytes": 277926457, "write_bytes": 2116814672},
-    "conv_2stage#1": {"src": "8cfb246101a56548", "fetch_bytes": 2112059975, "write_bytes": 133777088},
-    "convT_2stage#0": {"src": "19c24d078ac3a25f", "fetch_bytes": 140768833, "write_bytes": 1282602000},
-    "convT_2stage#1": {"src": "19c24d078ac3a25f", "fetch_bytes": 1223686229, "write_bytes": 1121160960},
+    "conv": {"src": "3a907b7630850971", "fetch_bytes": 266680166, "write_bytes": 130634688},
+    "conv_bf16": {"src": "3a907b7630850971", "fetch_bytes": 136599629, "write_bytes": 81045248},
+    "maxpool": {"src": "7fe7bbddd12793d9", "fetch_bytes": 2160266671, "write_bytes": 2140676160},
+    "maxpool_s2": {"src": "7fe7bbddd12793d9", "fetch_bytes": 2176842153, "write_bytes": 536870912},
+    "maxpool_d2": {"src": "7fe7bbddd12793d9", "fetch_bytes": 2266872936, "write_bytes": 2147483648},
+    "convT": {"src": "d41d08fdc4635d00", "fetch_bytes": 141522867, "write_bytes": 1255659040},
+    "convT_bf16": {"src": "712a7c1de94f1105", "fetch_bytes": 77389962, "write_bytes": 772873088},
+    "conv_general": {"src": "456ad05d0ed2d488", "fetch_bytes": 137068798, "write_bytes": 69234304},
+    "conv_2stage#0": {"src": "8cfb246101a56548", "fetch_bytes": 278848234, "write_bytes": 2116945920},
+    "conv_2stage#1": {"src": "8cfb246101a56548", "fetch_bytes": 2112062932, "write_bytes": 133776496},
+    "convT_2stage#0": {"src": "98a24a537c00e58f", "fetch_bytes": 140929669, "write_bytes": 1282896784},
+    "convT_2stage#1": {"src": "98a24a537c00e58f", "fetch_bytes": 1223682156, "write_bytes": 1121247296},
 }
 KERNEL_SOURCES = {
     "conv": ["conv_pool.hip", "ps_internal.h"],
