@@ -139,8 +139,8 @@ int ps_conv2d(const void *x, const void *w, const float *bias, void *y, int dtyp
  *   floor mode.  The result is bit-exact (a max of the inputs).
  * x [N,C,H,W] float32, y [N,C,OH,OW] float32.  stride <= 0 means stride = k.
  * NaN inputs are outside the contract (the result may or may not carry them).
- * Supported: 1 <= k <= 16, 1 <= dil, 0 <= pad, any stride >= 1, OH <= 65535 for
- * stride > 1 (524280 for stride 1),
+ * Supported: any k >= 1, 1 <= dil, 0 <= pad with H + 2*pad and W + 2*pad below
+ * 2^31, any stride >= 1, OH <= 65535 for stride > 1 (524280 for stride 1),
  * H*W < 2^31. */
 int ps_maxpool2d(const float *x, float *y, int N, int C, int H, int W, int k, int stride,
                  int pad, int dil, void *stream);

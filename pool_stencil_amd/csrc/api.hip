@@ -90,7 +90,9 @@ int ps_maxpool2d(const float *x, float *y, int N, int C, int H, int W, int k, in
     st = ps_pool2d_out_dim(W, k, stride, pad, dil, &OW);
     if (st != PS_OK) return st;
     if (too_big(N, C, H, W) || too_big(N, C, OH, OW)) return PS_ERR_SHAPE;
-    if (k > 16) return PS_ERR_UNSUPPORTED;
+    // window rows and columns are 32-bit indices in -pad .. H + pad - 1
+    if ((int64_t)H + 2 * (int64_t)pad > 0x7fffffff || (int64_t)W + 2 * (int64_t)pad > 0x7fffffff)
+        return PS_ERR_UNSUPPORTED;
     if (!aligned16(x) || !aligned16(y)) return PS_ERR_ALIGN;
     return ps::launch_maxpool2d(x, y, N, C, H, W, OH, OW, k, stride, pad, dil,
                                 (hipStream_t)stream);

@@ -133,6 +133,8 @@ static void entry_points(void) {
     EXPECT(ps_maxpool2d(fA, (float *)M, 2, 3, 40, 50, 4, 1, 1, 1, NULL), PS_ERR_ALIGN);
     EXPECT(ps_maxpool2d(fA, fy, 2, 3, 40, 50, 4, 1, 1, 1, NULL), 77);
     EXPECT(ps_maxpool2d(fA, fy, 2, 3, 40, 50, 3, -1, 1, 2, NULL), 77);
+    EXPECT(ps_maxpool2d(fA, fy, 2, 3, 40, 50, 20, 3, 5, 1, NULL), 77);
+    EXPECT(ps_maxpool2d(fA, fy, 1, 1, 8, 8, 3, 1 << 20, 1 << 30, 1, NULL), PS_ERR_UNSUPPORTED);
     /* transposed conv */
     EXPECT(ps_convT_softmax_bias_scale_sigmoid(fA, fA, NULL, NULL, fy, 2, 64, 8, 8, 128, 4, 2, 1, 1, 1, 2.f, NULL), PS_ERR_NULL);
     EXPECT(ps_convT_softmax_bias_scale_sigmoid(fA, fA, NULL, fA, fy, 2, 64, 8, 8, 128, 3, 2, 1, 1, 1, 2.f, NULL), PS_ERR_UNSUPPORTED);
@@ -151,7 +153,7 @@ static void entry_points(void) {
     EXPECT(ps_softmax_bias_scale_sigmoid(fA, fA, fy, 2, 128, 9, 9, 2.f, NULL), 77);
     EXPECT(ps_softmax_bias_scale_sigmoid(fA, NULL, fy, 2, 128, 9, 9, 2.f, NULL), PS_ERR_NULL);
 #undef EXPECT
-    CHECK(ps_stub_calls - calls == 12, "accepted calls reaching a launcher: %d", ps_stub_calls - calls);
+    CHECK(ps_stub_calls - calls == 13, "accepted calls reaching a launcher: %d", ps_stub_calls - calls);
     for (int st = -1; st <= 8; ++st) CHECK(ps_status_string(st) != NULL, "status string %d", st);
 }
 

@@ -170,7 +170,8 @@ def test_maxpool_validation(ps):
     assert _pool(lib, k=0) == ps.PS_ERR_PARAM
     assert _pool(lib, p=-1) == ps.PS_ERR_PARAM
     assert _pool(lib, H=2, p=0) == ps.PS_ERR_SHAPE
-    assert _pool(lib, k=17, H=40, W=40) == ps.PS_ERR_UNSUPPORTED
+    # a padding that takes window indices past 32 bits (a large stride keeps OH small)
+    assert _pool(lib, H=8, W=8, k=3, s=1 << 20, p=1 << 30) == ps.PS_ERR_UNSUPPORTED
     assert _pool(lib, y=MISALIGNED) == ps.PS_ERR_ALIGN
     assert _pool(lib, N=1 << 20, C=1 << 20) == ps.PS_ERR_SHAPE   # > 2^40 elements
 

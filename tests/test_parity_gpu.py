@@ -78,7 +78,9 @@ POOL_CASES = [
     (2, 3, 64, 64, 2, 2, 0, 1),
     (1, 1, 20, 300, 5, 3, 2, 1),
     (1, 2, 9, 9, 1, 1, 0, 1),       # k = 1: the identity
-    (1, 1, 30, 31, 16, 5, 8, 1),    # the largest window
+    (1, 1, 30, 31, 16, 5, 8, 1),
+    (1, 2, 50, 45, 20, 3, 5, 1),    # windows beyond 16: runtime-k kernel
+    (1, 1, 60, 60, 17, 2, 8, 2),    # k 17 dilated: a 33-wide window
     (1, 70000, 4, 4, 2, 2, 0, 1),   # more planes than one grid dimension holds
     # strided / dilated row-streaming kernel: several bands and strips
     (1, 2, 150, 600, 3, 2, 1, 1),   # k3 s2: 3 bands of 32 rows, 2 strips
