@@ -95,7 +95,8 @@ struct TileGeom {
 #define PS_CONV_MIN_WAVES 3
 #endif
 
-template <int PK, int NPW, int CING>
+// NCT: 16-channel tiles per workgroup pass (4, or 1 when Cout <= 16)
+template <int PK, int NPW, int CING, int NCT>
 __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? PS_CONV_MIN_WAVES : 1)) void conv_pool_f32(
     const float *__restrict__ x, const float *__restrict__ w, const float *__restrict__ cb,
     const float *__restrict__ b2, float *__restrict__ y, int Cin, int H, int W, int Cout,
@@ -122,14 +123,14 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? PS_CONV_MIN_WAVES : 1)) void c
     // minimum of the conv sums, so the pool loop is a plain max (no multiply per value).
     const float sgn = scale < 0.f ? -1.f : 1.f;
     const uint32_t sgn_bit = scale < 0.f ? 0x80000000u : 0u;
-    float wr[4][9][CING];
+    float wr[NCT][9][CING];
     auto load_weights = [&](int ct) {
         // Every weight of the tile present and scale >= 0 (a uniform test): plain loads,
         // without the per-weight select and sign flip (144 VALU instructions per wave,
         // which the matrix cores would wait for).
-        if (sgn_bit == 0u && Cin == CINP && ct + 64 <= Cout) {
+        if (sgn_bit == 0u && Cin == CINP && ct + 16 * NCT <= Cout) {
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt)
+            for (int nt = 0; nt < NCT; ++nt)
 #pragma unroll
                 for (int g = 0; g < CING; ++g) {
                     const float *wp = w + ((size_t)(ct + 16 * nt + j) * Cin + 4 * g + g4) * 9;
@@ -139,7 +140,7 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? PS_CONV_MIN_WAVES : 1)) void c
             return;
         }
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
+        for (int nt = 0; nt < NCT; ++nt) {
             const int co = ct + 16 * nt + j;
 #pragma unroll
             for (int g = 0; g < CING; ++g) {
@@ -337,16 +338,16 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? PS_CONV_MIN_WAVES : 1)) void c
     const uint32_t lane_off =
         pw < PW ? 4u * ((uint32_t)(4 * g4) * cplane + (uint32_t)(ph * PW + pw)) : 0x80000000u;
 
-    for (int ct = 0; ct < Cout; ct += 64) {
+    for (int ct = 0; ct < Cout; ct += 16 * NCT) {
         if (ct > 0) {
             __syncthreads();  // every wave is done with the previous tile's biases
             stage_bias(ct);
             load_weights(ct);
             __syncthreads();
         }
-        f32x4 best[4];
+        f32x4 best[NCT];
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) best[nt] = (f32x4){-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+        for (int nt = 0; nt < NCT; ++nt) best[nt] = (f32x4){-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 
 #pragma unroll 1
         for (int dy = 0; dy < PK; ++dy) {
@@ -359,9 +360,9 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? PS_CONV_MIN_WAVES : 1)) void c
             for (int dk = 0; dk < DXG; ++dk) {
                 const int dx = dx0 + dk;
                 if (DXG < PK && dx >= PK) break;
-                f32x4 acc[4];
+                f32x4 acc[NCT];
 #pragma unroll
-                for (int nt = 0; nt < 4; ++nt) acc[nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+                for (int nt = 0; nt < NCT; ++nt) acc[nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int g = 0; g < CING; ++g)
 #pragma unroll
@@ -371,12 +372,12 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? PS_CONV_MIN_WAVES : 1)) void c
                             const int t = dx + kw;
                             const float b = tr[g * 4 * PS + kh * G::RSF + (t % PK) * G::QF + t / PK];
 #pragma unroll
-                            for (int nt = 0; nt < 4; ++nt)
+                            for (int nt = 0; nt < NCT; ++nt)
                                 acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(
                                     wr[nt][kh * 3 + kw][g], b, acc[nt], 0, 0, 0);
                         }
 #pragma unroll
-                for (int nt = 0; nt < 4; ++nt)
+                for (int nt = 0; nt < NCT; ++nt)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) best[nt][r] = fmaxf(best[nt][r], acc[nt][r]);
             }
@@ -388,7 +389,7 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? PS_CONV_MIN_WAVES : 1)) void c
         // are dropped without branches (the host keeps (Cout + 64) planes below 2^31
         // bytes, so no offset wraps).
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
+        for (int nt = 0; nt < NCT; ++nt)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int cl = 16 * nt + 4 * g4 + r;
@@ -862,13 +863,17 @@ int launch_pk_npw(const void *x, const void *w, const float *cb, const float *b2
     const uint64_t nblocks = (uint64_t)N * PH * npwt;
     if (nblocks > 0x7fffffffull) return PS_ERR_UNSUPPORTED;
     const dim3 grid((unsigned)nblocks), block(64 * NPW);
-    if (Cin <= 4)
-        return launch(conv_pool_f32<PK, NPW, 1>, grid, block, 0, stream, (const float *)x,
-                      (const float *)w, cb, b2, (float *)y, Cin, H, W, Cout, pad, PH, PW, scale,
-                      npwt);
-    return launch(conv_pool_f32<PK, NPW, 2>, grid, block, 0, stream, (const float *)x,
-                  (const float *)w, cb, b2, (float *)y, Cin, H, W, Cout, pad, PH, PW, scale,
-                  npwt);
+#define PS_F32_LAUNCH(CG, NCT)                                                                 \
+    launch(conv_pool_f32<PK, NPW, CG, NCT>, grid, block, 0, stream, (const float *)x,           \
+           (const float *)w, cb, b2, (float *)y, Cin, H, W, Cout, pad, PH, PW, scale, npwt)
+    // one 16-channel tile when Cout <= 16 (narrow strips only: the small problems), so
+    // no matrix work is spent on channels that do not exist
+    if constexpr (NPW == 1) {
+        if (Cout <= 16) return Cin <= 4 ? PS_F32_LAUNCH(1, 1) : PS_F32_LAUNCH(2, 1);
+    }
+    if (Cin <= 4) return PS_F32_LAUNCH(1, 4);
+    return PS_F32_LAUNCH(2, 4);
+#undef PS_F32_LAUNCH
 }
 
 template <int PK>
