@@ -72,18 +72,18 @@ TINY_FLOP = 2 * 72 * 2 * 16 * 28 * 28              # the 28x28 conv outputs the 
 # x1.0.  `src` is the hash of the kernel's sources when the counters were taken; a
 # kernel edited since then reports traffic null.  See profiles/traffic_*.md.
 TRAFFIC = {
-    "conv": {"src": "3a907b7630850971", "fetch_bytes": 266680166, "write_bytes": 130634688},
-    "conv_bf16": {"src": "3a907b7630850971", "fetch_bytes": 136599629, "write_bytes": 81045248},
-    "maxpool": {"src": "7fe7bbddd12793d9", "fetch_bytes": 2160266671, "write_bytes": 2140676160},
-    "maxpool_s2": {"src": "7fe7bbddd12793d9", "fetch_bytes": 2176842153, "write_bytes": 536870912},
-    "maxpool_d2": {"src": "7fe7bbddd12793d9", "fetch_bytes": 2266872936, "write_bytes": 2147483648},
-    "convT": {"src": "d41d08fdc4635d00", "fetch_bytes": 141522867, "write_bytes": 1255659040},
-    "convT_bf16": {"src": "712a7c1de94f1105", "fetch_bytes": 77389962, "write_bytes": 772873088},
-    "conv_general": {"src": "456ad05d0ed2d488", "fetch_bytes": 137068798, "write_bytes": 69234304},
-    "conv_2stage#0": {"src": "8cfb246101a56548", "fetch_bytes": 278848234, "write_bytes": 2116945920},
-    "conv_2stage#1": {"src": "8cfb246101a56548", "fetch_bytes": 2112062932, "write_bytes": 133776496},
-    "convT_2stage#0": {"src": "98a24a537c00e58f", "fetch_bytes": 140929669, "write_bytes": 1282896784},
-    "convT_2stage#1": {"src": "98a24a537c00e58f", "fetch_bytes": 1223682156, "write_bytes": 1121247296},
+    "conv": {"src": "acd53f66d671af14", "fetch_bytes": 266692295, "write_bytes": 130649232},
+    "conv_bf16": {"src": "acd53f66d671af14", "fetch_bytes": 136587260, "write_bytes": 81220448},
+    "maxpool": {"src": "7fe7bbddd12793d9", "fetch_bytes": 2160265384, "write_bytes": 2140676736},
+    "maxpool_s2": {"src": "7fe7bbddd12793d9", "fetch_bytes": 2176862295, "write_bytes": 536870912},
+    "maxpool_d2": {"src": "7fe7bbddd12793d9", "fetch_bytes": 2266569258, "write_bytes": 2147483648},
+    "convT": {"src": "d41d08fdc4635d00", "fetch_bytes": 141249703, "write_bytes": 1256486288},
+    "convT_bf16": {"src": "712a7c1de94f1105", "fetch_bytes": 77606485, "write_bytes": 773801136},
+    "conv_general": {"src": "456ad05d0ed2d488", "fetch_bytes": 137132587, "write_bytes": 69301104},
+    "conv_2stage#0": {"src": "8cfb246101a56548", "fetch_bytes": 276390802, "write_bytes": 2116707312},
+    "conv_2stage#1": {"src": "8cfb246101a56548", "fetch_bytes": 2112061737, "write_bytes": 133770352},
+    "convT_2stage#0": {"src": "98a24a537c00e58f", "fetch_bytes": 141007151, "write_bytes": 1282438560},
+    "convT_2stage#1": {"src": "98a24a537c00e58f", "fetch_bytes": 1223700946, "write_bytes": 1121319552},
 }
 KERNEL_SOURCES = {
     "conv": ["conv_pool.hip", "ps_internal.h"],
