@@ -61,8 +61,25 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed for: " + ", ".join(failed))
     tmp = LIB + f".tmp{os.getpid()}"
     subprocess.check_call([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp])
+    # The host pass can leave a kernel's launch handle undefined without any diagnostic
+    # (seen with a lambda call passed straight to the LDS-DMA load builtin); the library
+    # then fails only when it is loaded.  Refuse such a library here.
+    undefined = _undefined_own_symbols(tmp)
+    if undefined:
+        os.remove(tmp)
+        raise RuntimeError("library leaves its own symbols undefined: " + ", ".join(undefined))
     os.replace(tmp, LIB)
     return LIB
+
+
+def _undefined_own_symbols(lib: str) -> list:
+    """Undefined dynamic symbols of the library that belong to its own namespace (ps::)."""
+    try:
+        out = subprocess.run(["nm", "-D", "--undefined-only", lib], capture_output=True,
+                             text=True, check=True).stdout
+    except (OSError, subprocess.CalledProcessError):
+        return []  # no nm: the load-time check in the binding still catches it
+    return [l.split()[-1] for l in out.splitlines() if l.split() and l.split()[-1].startswith("_ZN2ps")]
 
 
 if __name__ == "__main__":

@@ -409,7 +409,7 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? PS_CONV_MIN_WAVES : 1)) void c
 // rows that pooled row ph+1 adds are loaded from HBM during the MFMA work of row ph
 // (into an LDS staging area when rows are 16-byte aligned, else into registers) and
 // transposed into the ring afterwards.  One barrier per row.
-template <int PK, int NPW, bool VEC, bool MULTI, bool W32>
+template <int PK, int NPW, bool VEC, bool MULTI>
 __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? 2 : 1)) void conv_pool_bf16(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, const float *__restrict__ cb,
     const float *__restrict__ b2, uint16_t *__restrict__ y, int Cin, int H, int W, int Cout,
@@ -526,35 +526,6 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? 2 : 1)) void conv_pool_bf16(
             }
         }
     };
-    // W32 (v_mfma_f32_32x32x16_bf16, one 64-channel tile): wave wv owns channels
-    // 32*(wv & 1) .. +31 and pooled columns 32*(wv >> 1) .. +31 of the strip; lane l
-    // is pixel (B/D column) l & 31 and, as A row, channel 32*(wv & 1) + (l & 31).  K-step
-    // s (0..4) = kernel taps 2s, 2s+1 x 8 channels, lane half h = l >> 5 taking tap 2s + h
-    // (tap 9 carries zero weights): 80 K per window position instead of 96, and half
-    // as many matrix instructions, each twice as large, as the 16x16x32 form.
-    const int h32 = lane >> 5, n32 = lane & 31;
-    const int cw32 = wv & 1, px32 = wv >> 1;
-    bf16x8 wa32[W32 ? 5 : 1];
-    auto load_weights32 = [&]() {
-        const int co = 32 * cw32 + n32;
-#pragma unroll
-        for (int s = 0; s < (W32 ? 5 : 1); ++s) {
-            const int tap = 2 * s + h32;
-            uint32_t hv[8];
-#pragma unroll
-            for (int ci = 0; ci < 8; ++ci) {
-                const bool ok = co < Cout && ci < Cin && tap < 9;
-                const uint32_t v = w[ok ? ((size_t)co * Cin + ci) * 9 + tap : 0];
-                hv[ci] = ok ? v : 0u;
-            }
-            uint4 pk;
-            pk.x = (hv[0] | (hv[1] << 16)) ^ wsign;
-            pk.y = (hv[2] | (hv[3] << 16)) ^ wsign;
-            pk.z = (hv[4] | (hv[5] << 16)) ^ wsign;
-            pk.w = (hv[6] | (hv[7] << 16)) ^ wsign;
-            wa32[s] = __builtin_bit_cast(bf16x8, pk);
-        }
-    };
     // Epilogue constants: with u = sgn*best + cb, tanh(u) = 1 - 2/(2^(2u log2e) + 1), so
     // out = (scale + b2) - 2 scale / (2^(best*k2 + cb*2log2e) + 1), k2 = 2 log2e sgn.
     constexpr float kTwoLog2e = 2.8853900817779268f;
@@ -582,16 +553,16 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? 2 : 1)) void conv_pool_bf16(
         }
     }
 
-    // Per lane, K-step s covers kernel tap 4*s + g4 (W32: 2*s + h32); taps >= 9 carry
+    // Per lane, K-step s covers kernel tap 4*s + g4; taps >= 9 carry
     // zero weights and read a valid in-ring entry.  Column part of the ring offset per
     // (s, dx), and the lane's pooled column within the strip.
-    constexpr int NS = W32 ? 5 : 3;
-    const int pwl = W32 ? 32 * px32 + n32 : 16 * wv + j;
+    constexpr int NS = 3;
+    const int pwl = 16 * wv + j;
     int coff[NS][PK];
     int khs[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-        const int tap = min(W32 ? 2 * s + h32 : 4 * s + g4, 8);
+        const int tap = min(4 * s + g4, 8);
         const int kh = tap / 3, kw = tap % 3;
         khs[s] = kh;
 #pragma unroll
@@ -610,16 +581,12 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? 2 : 1)) void conv_pool_bf16(
     const uint32_t cplane = (uint32_t)(PH * PW);
     const __amdgpu_buffer_rsrc_t yr =
         make_range_checked(y + (size_t)n * Cout * cplane, 2u * (uint32_t)Cout * cplane);
-    // (the lane's first channel: 4*g4, W32 32*(wv & 1) + 4*h32)
-    const uint32_t lane_c0 = W32 ? 32 * cw32 + 4 * h32 : 4 * g4;
+    const uint32_t lane_c0 = 4 * g4;  // the lane's first channel
     const uint32_t lane_off = pw < PW ? 2u * (lane_c0 * cplane + (uint32_t)pw) : 0x80000000u;
     // MULTI: Cout > 64, the weights and biases of each 64-channel tile are reloaded per row
     constexpr bool single_tile = !MULTI;
     if constexpr (single_tile) {
-        if constexpr (W32)
-            load_weights32();
-        else
-            load_weights(0);
+        load_weights(0);
         stage_bias(0);
     }
     __syncthreads();
@@ -685,12 +652,11 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? 2 : 1)) void conv_pool_bf16(
             // position p's first MFMAs, when their results are long complete.
             constexpr int NPOS = PK * PK;
             constexpr int NFR = NS * NPOS;
-            constexpr int AHEAD_REQ = W32 ? PS_BF16_W32_AHEAD
-                                      : (MULTI || !VEC) && PS_BF16_LDS_AHEAD > 2 ? 2 : PS_BF16_LDS_AHEAD;
+            constexpr int AHEAD_REQ = (MULTI || !VEC) && PS_BF16_LDS_AHEAD > 2 ? 2 : PS_BF16_LDS_AHEAD;
             constexpr int AHEAD = AHEAD_REQ < NFR ? AHEAD_REQ : NFR;
             // the variants with more live registers (row loads held in registers, or
             // several channel tiles) take the pool max at the first K-step
-            constexpr int MAX_STEP = W32 ? 2 : (MULTI || !VEC) ? 0 : PS_BF16_MAX_STEP;
+            constexpr int MAX_STEP = (MULTI || !VEC) ? 0 : PS_BF16_MAX_STEP;
             int ridx[NS][PK];  // ring entry index of kernel row khs[s] for window row dy
             {
                 const int rb = ((rbase % RING) + RING) % RING;
@@ -709,56 +675,6 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? 2 : 1)) void conv_pool_bf16(
             bf16x8 bq[AHEAD];
 #pragma unroll
             for (int f = 0; f < AHEAD; ++f) bq[f] = frag(f);
-            if constexpr (W32) {
-                // D (32x32): lane l, register r = channel 32*(wv & 1) + 8*(r/4) + 4*h32 + r%4
-                // of the tile, pooled column pwl.  Positions as above, five K-steps each.
-                f32x16 best;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) best[r] = -INFINITY;
-                f32x16 acc[3];
-#pragma unroll
-                for (int f = 0; f < NFR; ++f) {
-                    const int pp = f / NS, s = f % NS;
-                    const bf16x8 b = bq[f % AHEAD];
-                    if (f + AHEAD < NFR) bq[f % AHEAD] = frag(f + AHEAD);
-                    acc[pp % 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        wa32[s], b, s == 0 ? (f32x16){} : acc[pp % 3], 0, 0, 0);
-                    if (s == MAX_STEP && pp >= 2 && pp % 2 == 0) {
-#pragma unroll
-                        for (int r = 0; r < 16; ++r)
-                            best[r] = fmaxf(fmaxf(best[r], acc[(pp - 2) % 3][r]), acc[(pp - 1) % 3][r]);
-                        asm volatile("" : "+v"(best));
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    if constexpr (NPOS % 2 == 0)
-                        best[r] = fmaxf(fmaxf(best[r], acc[(NPOS - 2) % 3][r]), acc[(NPOS - 1) % 3][r]);
-                    else
-                        best[r] = fmaxf(best[r], acc[(NPOS - 1) % 3][r]);
-                }
-                if (more) refill();
-                // output (n, co = 32*(wv & 1) + 8*(r/4) + 4*h32 + r%4, ph, pw)
-                const uint32_t row_off = lane_off + 2u * (uint32_t)(ph * PW);
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int c0 = 32 * cw32 + 8 * q + 4 * h32;
-                    const float4 cbv = *(const float4 *)&s_bias[0][c0];
-                    const float4 c2v = *(const float4 *)&s_bias[1][c0];
-                    const float cbr[4] = {cbv.x, cbv.y, cbv.z, cbv.w};
-                    const float c2r[4] = {c2v.x, c2v.y, c2v.z, c2v.w};
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float e = __builtin_amdgcn_exp2f(fmaf(best[4 * q + r], k2, cbr[r]));
-                        const float o = fmaf(m2, __builtin_amdgcn_rcpf(e + 1.f), c2r[r]);
-                        __builtin_amdgcn_raw_buffer_store_b16(
-                            f32_to_bf16_rne(o), yr, (int)(row_off + 2u * (uint32_t)(8 * q + r) * cplane),
-                            0, 0);
-                    }
-                }
-                continue;
-            }
             f32x4 best[4];
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) best[nt] = (f32x4){-INFINITY, -INFINITY, -INFINITY, -INFINITY};
@@ -826,38 +742,303 @@ __global__ __launch_bounds__(64 * NPW, (PK <= 4 ? 2 : 1)) void conv_pool_bf16(
     }
 }
 
+// bf16, one 64-channel tile, pool <= 4, rows 16-byte aligned: v_mfma_f32_32x32x16_bf16.
+// Persistent like the kernel above (a run of pooled rows of one strip per workgroup,
+// weights loaded once), with:
+//   - a ring of 2*PK input rows: after each pooled row's matrix work a barrier, then the
+//     next row's PK new rows (already in the LDS staging area) overwrite the two oldest
+//     rows of the current one, then a second barrier;
+//   - pooled rows processed in pairs, so the ring slot of every B fragment is known at
+//     compile time: a fragment address is one of a few per-lane bases plus an immediate
+//     offset, with no per-row address arithmetic;
+//   - a staging area that holds only the 8-column groups in use (stage[wave][channel]
+//     [group of the wave]).
+// At pool 4 and 64 columns: 141 VGPRs and 50.7 KB of LDS (with a 2*PK + 2 row ring and
+// per-row addresses: 194 VGPRs, 74 KB).  Three workgroups would fit a CU, but it is
+// launched with two: a 63-row plane splits into 4 runs of 15-16 rows, and into 6 runs of
+// 10-11 rows the longest run is 5% above the mean, which cost more than the third
+// workgroup's latency hiding gained on the conv+pool workload.
+template <int PK, int NPW>
+__global__ __launch_bounds__(64 * NPW, 3) void conv_pool_bf16_w32(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, const float *__restrict__ cb,
+    const float *__restrict__ b2, uint16_t *__restrict__ y, int Cin, int H, int W, int Cout,
+    int pad, int PH, int PW, float scale, int npwt, int nseg) {
+    using G = TileGeom<PK, NPW>;
+    constexpr int NT = 64 * NPW;
+    constexpr int RING = 2 * PK;             // input rows held in LDS
+    constexpr int NG = (G::COLS + 7) / 8;    // 8-column groups per tile row
+    constexpr int NTOT = PK * NG;            // groups of the PK rows a pooled row adds
+    constexpr int IPW = (NTOT + NPW - 1) / NPW;  // of them per wave
+    static_assert(IPW <= 64, "one group per lane");
+    static_assert(RING * G::RS * 16 < 65536, "fragment offsets fit the LDS offset field");
+    __shared__ uint4 ring[RING * G::RS];
+    __shared__ uint4 stage[NPW][8][IPW];
+    __shared__ float s_bias[2][64];
+    const int wvu = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+    // ---- work item: (image n, column strip pwt, pooled rows [p0, p1)) ----
+    const uint32_t L = xcd_remap(blockIdx.x, gridDim.x);
+    const int seg = (int)(L % (uint32_t)nseg);
+    const int pwt = (int)((L / (uint32_t)nseg) % (uint32_t)npwt);
+    const int n = (int)(L / ((uint32_t)nseg * (uint32_t)npwt));
+    const int p0 = (int)(((int64_t)PH * seg) / nseg);
+    const int p1 = (int)(((int64_t)PH * (seg + 1)) / nseg);
+
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+    const int ic0 = PK * pwt * G::T - pad;
+    const int r0 = PK * p0 - pad;  // input row in ring slot 0
+    const uint16_t *xn = x + (size_t)n * Cin * H * W;
+    const uint32_t cstride = (uint32_t)H * (uint32_t)W;
+    const __amdgpu_buffer_rsrc_t xr = make_range_checked(xn, 2u * (uint32_t)Cin * cstride);
+    // byte offset of input (row ir, column ic) of channel ci, or a masked offset (reads 0)
+    auto in_off = [&](int ir, int ic, int ci) {
+        const bool ok = (ir >= 0) & (ir < H) & (ci < Cin) & (ic >= 0) & (ic < W);
+        return ok ? 2u * ((uint32_t)ci * cstride + (uint32_t)(ir * W + ic)) : 0x80000000u;
+    };
+    // Transpose an 8x8 block (channel x column: 8 columns of each channel) and write the
+    // 8 channel-last entries of input row ir, group u.
+    auto store_group = [&](int ir, int u, const uint4 (&v)[8]) {
+        uint4 *rrow = ring + ((ir - r0) % RING) * G::RS;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int c = 8 * u + k;
+            const uint32_t sel = (k & 1) ? 0x07060302u : 0x05040100u;
+            uint32_t wd[8];
+#pragma unroll
+            for (int ci = 0; ci < 8; ++ci)
+                wd[ci] = (k >> 1) == 0 ? v[ci].x : (k >> 1) == 1 ? v[ci].y
+                       : (k >> 1) == 2 ? v[ci].z : v[ci].w;
+            if (c < G::COLS)
+                rrow[(c % PK) * G::Q + c / PK] =
+                    make_uint4(__builtin_amdgcn_perm(wd[1], wd[0], sel), __builtin_amdgcn_perm(wd[3], wd[2], sel),
+                               __builtin_amdgcn_perm(wd[5], wd[4], sel), __builtin_amdgcn_perm(wd[7], wd[6], sel));
+        }
+    };
+
+    // Wave wv owns channels 32*(wv & 1) .. +31 and pooled columns 32*(wv >> 1) .. +31 of
+    // the strip; lane l is pixel (B/D column) l & 31 and, as A row, channel
+    // 32*(wv & 1) + (l & 31).  K-step s (0..4) = kernel taps 2s, 2s+1 x 8 channels, lane
+    // half h = l >> 5 taking tap 2s + h (tap 9 carries zero weights).
+    const int h32 = lane >> 5, n32 = lane & 31;
+    const int cw32 = wv & 1, px32 = wv >> 1;
+    const uint32_t wsign = scale < 0.f ? 0x80008000u : 0u;
+    bf16x8 wa32[5];
+    {
+        const int co = 32 * cw32 + n32;
+#pragma unroll
+        for (int s = 0; s < 5; ++s) {
+            const int tap = 2 * s + h32;
+            uint32_t hv[8];
+#pragma unroll
+            for (int ci = 0; ci < 8; ++ci) {
+                const bool ok = co < Cout && ci < Cin && tap < 9;
+                const uint32_t v = w[ok ? ((size_t)co * Cin + ci) * 9 + tap : 0];
+                hv[ci] = ok ? v : 0u;
+            }
+            // negative scale: negate the weights (exact), so the window max of the
+            // negated sums is minus the window min of the sums
+            uint4 pk;
+            pk.x = (hv[0] | (hv[1] << 16)) ^ wsign;
+            pk.y = (hv[2] | (hv[3] << 16)) ^ wsign;
+            pk.z = (hv[4] | (hv[5] << 16)) ^ wsign;
+            pk.w = (hv[6] | (hv[7] << 16)) ^ wsign;
+            wa32[s] = __builtin_bit_cast(bf16x8, pk);
+        }
+    }
+    // with u = sgn*best + cb, tanh(u) = 1 - 2/(2^(2u log2e) + 1), so
+    // out = (scale + b2) - 2 scale / (2^(best*k2 + cb*2log2e) + 1), k2 = 2 log2e sgn
+    constexpr float kTwoLog2e = 2.8853900817779268f;
+    if (threadIdx.x < 64) {
+        const int co = threadIdx.x;
+        s_bias[0][threadIdx.x] = (co < Cout && cb) ? cb[co] * kTwoLog2e : 0.f;
+        s_bias[1][threadIdx.x] = co < Cout ? scale + b2[co] : 0.f;
+    }
+
+    // ---- prologue: the PK + 2 input rows of pooled row p0, into slots 0 .. PK + 1 ----
+    if (p0 < p1) {
+        constexpr int TOTAL = (PK + 2) * NG;
+        constexpr int PER = (TOTAL + NT - 1) / NT;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int e = threadIdx.x + i * NT;
+            if (e < TOTAL) {
+                const int ir = r0 + e / NG, ic = ic0 + 8 * (e % NG);
+                uint4 v[8];
+#pragma unroll
+                for (int ci = 0; ci < 8; ++ci)
+                    v[ci] = __builtin_bit_cast(
+                        uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, in_off(ir, ic, ci), 0, 0));
+                store_group(ir, e % NG, v);
+            }
+        }
+    }
+
+    const int pwl = 32 * px32 + n32;  // the lane's pooled column within the strip
+    const int pw = pwt * G::T + pwl;
+    const float k2 = scale < 0.f ? -kTwoLog2e : kTwoLog2e;
+    const float m2 = -2.f * scale;
+    // Output stores go through a range-checked resource over image n's Cout planes: a
+    // store at or past its end is dropped (channels >= Cout); columns pw >= PW take an
+    // offset far past the end (the host keeps (Cout + 64) planes under 2^31 bytes).
+    const uint32_t cplane = (uint32_t)(PH * PW);
+    const __amdgpu_buffer_rsrc_t yr =
+        make_range_checked(y + (size_t)n * Cout * cplane, 2u * (uint32_t)Cout * cplane);
+    const uint32_t lane_off =
+        pw < PW ? 2u * ((uint32_t)(32 * cw32 + 4 * h32) * cplane + (uint32_t)pw) : 0x80000000u;
+    // this thread's group of the PK new rows: e = wave * IPW + lane
+    const int fe = wvu * IPW + lane;
+    const bool f_on = lane < IPW && fe < NTOT;
+    const int f_row = fe / NG, f_u = fe % NG;
+    const char *ringb = (const char *)ring;
+    const int lane16 = 16 * pwl;
+    // the wave's staging slots as an LDS pointer (the DMA loads' destination)
+    typedef __attribute__((address_space(3))) uint4 lds_uint4;
+    lds_uint4 *const stg = (lds_uint4 *)&stage[wvu][0][0];
+    __syncthreads();
+
+    // Pooled rows in pairs; phase = (ph - p0) mod 2 is a constant in each unrolled copy,
+    // so the row's input rows r0 + PK*(ph - p0) + k sit in known ring slots
+    // (phase*PK + k) mod RING.
+    for (int ph0 = p0; ph0 < p1; ph0 += 2) {
+#pragma unroll
+    for (int phase = 0; phase < 2; ++phase) {
+        const int ph = ph0 + phase;
+        if (ph >= p1) break;
+        const bool more = ph + 1 < p1;
+        const int nr0 = PK * (ph + 1) - pad + 2;  // first new row of pooled row ph + 1
+        if (more && f_on) {
+            const int ir = nr0 + f_row, ic = ic0 + 8 * f_u;
+#pragma unroll
+            for (int ci = 0; ci < 8; ++ci) {
+                const uint32_t o = in_off(ir, ic, ci);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    xr, (__attribute__((address_space(3))) void *)(stg + ci * IPW), 16, o, 0, 0, 0);
+            }
+        }
+        // byte offset within the ring of entry (row k of this pooled row, tile column c)
+        auto eoff = [&](int k, int c) {
+            return ((phase * PK + k) % RING) * G::RS * 16 + ((c % PK) * G::Q + c / PK) * 16;
+        };
+        // B fragment f = (window position pp, K-step s): lane half h reads tap
+        // min(2s + h, 8) at (dy + kh, dx + kw); the half-1 difference is a per-lane
+        // constant, the rest an immediate offset
+        auto frag = [&](int f) {
+            const int pp = f / 5, s = f % 5, dy = pp / PK, dx = pp % PK;
+            const int t0 = 2 * s, t1 = 2 * s + 1 < 9 ? 2 * s + 1 : 8;
+            const int o0 = eoff(dy + t0 / 3, dx + t0 % 3);
+            const int o1 = eoff(dy + t1 / 3, dx + t1 % 3);
+            return *(const bf16x8 *)(ringb + (lane16 + (h32 ? o1 - o0 : 0)) + o0);
+        };
+        constexpr int NPOS = PK * PK;
+        constexpr int NFR = 5 * NPOS;
+        constexpr int AHEAD = PS_BF16_W32_AHEAD < NFR ? PS_BF16_W32_AHEAD : NFR;
+        bf16x8 bq[AHEAD];
+#pragma unroll
+        for (int f = 0; f < AHEAD; ++f) bq[f] = frag(f);
+        // D (32x32): lane l, register r = channel 32*(wv & 1) + 8*(r/4) + 4*h32 + r%4 of
+        // the tile, pooled column pwl.  Position p = dy*PK + dx accumulates into
+        // acc[p % 3]; the pool max of positions p-2 and p-1 (one v_max3 per value) is
+        // taken at position p's third K-step, when their results are long complete.
+        f32x16 best;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) best[r] = -INFINITY;
+        f32x16 acc[3];
+#pragma unroll
+        for (int f = 0; f < NFR; ++f) {
+            const int pp = f / 5, s = f % 5;
+            const bf16x8 b = bq[f % AHEAD];
+            if (f + AHEAD < NFR) bq[f % AHEAD] = frag(f + AHEAD);
+            acc[pp % 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                wa32[s], b, s == 0 ? (f32x16){} : acc[pp % 3], 0, 0, 0);
+            if (s == 2 && pp >= 2 && pp % 2 == 0) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    best[r] = fmaxf(fmaxf(best[r], acc[(pp - 2) % 3][r]), acc[(pp - 1) % 3][r]);
+                // an empty volatile asm that takes the maxima as operands keeps them in
+                // this step (sunk to the end they would hold every position's sums live)
+                asm volatile("" : "+v"(best));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            if constexpr (NPOS % 2 == 0)
+                best[r] = fmaxf(fmaxf(best[r], acc[(NPOS - 2) % 3][r]), acc[(NPOS - 1) % 3][r]);
+            else
+                best[r] = fmaxf(best[r], acc[(NPOS - 1) % 3][r]);
+        }
+        __syncthreads();  // every wave is done reading this row's ring slots
+        if (more && f_on) {
+            // the new rows go to slots ((phase + 1)*PK + 2 + i) mod RING, two of which
+            // held this row's first two input rows
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's loads have landed
+            uint4 v[8];
+#pragma unroll
+            for (int ci = 0; ci < 8; ++ci) v[ci] = stage[wvu][ci][lane];
+            store_group(nr0 + f_row, f_u, v);
+        }
+        // output (n, co = 32*(wv & 1) + 8*(r/4) + 4*h32 + r%4, ph, pw)
+        const uint32_t row_off = lane_off + 2u * (uint32_t)(ph * PW);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int c0 = 32 * cw32 + 8 * q + 4 * h32;
+            const float4 cbv = *(const float4 *)&s_bias[0][c0];
+            const float4 c2v = *(const float4 *)&s_bias[1][c0];
+            const float cbr[4] = {cbv.x, cbv.y, cbv.z, cbv.w};
+            const float c2r[4] = {c2v.x, c2v.y, c2v.z, c2v.w};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float e = __builtin_amdgcn_exp2f(fmaf(best[4 * q + r], k2, cbr[r]));
+                const float o = fmaf(m2, __builtin_amdgcn_rcpf(e + 1.f), c2r[r]);
+                __builtin_amdgcn_raw_buffer_store_b16(
+                    f32_to_bf16_rne(o), yr, (int)(row_off + 2u * (uint32_t)(8 * q + r) * cplane), 0, 0);
+            }
+        }
+        __syncthreads();  // the ring holds pooled row ph + 1's rows; the stage is free
+    }
+    }
+}
+
 template <int PK, int NPW>
 int launch_pk_npw(const void *x, const void *w, const float *cb, const float *b2, void *y,
                   int dtype, int N, int Cin, int H, int W, int Cout, int pad, float scale, int PH,
                   int PW, hipStream_t stream) {
     const int npwt = (PW + 16 * NPW - 1) / (16 * NPW);
     if (dtype == PS_BF16) {
-        // persistent: about two workgroups per CU, each a run of pooled rows
+        // persistent workgroups, each a run of pooled rows of one strip, about two per CU
         int dev = 0, ncu = 0;
         if (hipGetDevice(&dev) != hipSuccess) return PS_ERR_HIP;
         if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             return PS_ERR_HIP;
+        // every strip starts at a multiple of 16*NPW*PK columns, so alignment is uniform
+        const bool vec = (pad % 8 == 0) && (W % 8 == 0);
+        const bool multi = Cout > 64;
+        // one channel tile, pool <= 4, 32 or 64 columns per strip and rows staged through
+        // LDS: the 32x32x16 form (with rows held in registers it would spill)
+        constexpr bool w32_ok = PK <= 4 && (NPW == 2 || NPW == 4);
+        const bool w32 = w32_ok && vec && !multi;
         const int64_t strips = (int64_t)N * npwt;
         int64_t nseg = (2 * (int64_t)ncu + strips - 1) / strips;
         if (nseg > PH) nseg = PH;
         if (nseg < 1) nseg = 1;
         const uint64_t nblocks = (uint64_t)strips * nseg;
         if (nblocks > 0x7fffffffull) return PS_ERR_UNSUPPORTED;
-        // every strip starts at a multiple of 16*NPW*PK columns, so alignment is uniform
-        const bool vec = (pad % 8 == 0) && (W % 8 == 0);
-        const bool multi = Cout > 64;
         const dim3 grid((unsigned)nblocks), block(64 * NPW);
-#define PS_BF16_LAUNCH(V, M, W32)                                                             \
-    launch(conv_pool_bf16<PK, NPW, V, M, W32>, grid, block, 0, stream, (const uint16_t *)x,   \
+        if constexpr (w32_ok) {
+            if (w32)
+                return launch(conv_pool_bf16_w32<PK, NPW>, grid, block, 0, stream,
+                              (const uint16_t *)x, (const uint16_t *)w, cb, b2, (uint16_t *)y, Cin,
+                              H, W, Cout, pad, PH, PW, scale, npwt, (int)nseg);
+        }
+#define PS_BF16_LAUNCH(V, M)                                                                  \
+    launch(conv_pool_bf16<PK, NPW, V, M>, grid, block, 0, stream, (const uint16_t *)x,        \
            (const uint16_t *)w, cb, b2, (uint16_t *)y, Cin, H, W, Cout, pad, PH, PW, scale,   \
            npwt, (int)nseg)
-        // one channel tile, pool <= 4, 32 or 64 columns per strip and rows staged through
-        // LDS: the 32x32x16 form (with rows held in registers it would spill)
-        constexpr bool w32 = PK <= 4 && (NPW == 2 || NPW == 4);
-        if (vec && !multi) return PS_BF16_LAUNCH(true, false, w32);
-        if (vec) return PS_BF16_LAUNCH(true, true, false);
-        if (!multi) return PS_BF16_LAUNCH(false, false, false);
-        return PS_BF16_LAUNCH(false, true, false);
+        if (vec && !multi) return PS_BF16_LAUNCH(true, false);
+        if (vec) return PS_BF16_LAUNCH(true, true);
+        if (!multi) return PS_BF16_LAUNCH(false, false);
+        return PS_BF16_LAUNCH(false, true);
 #undef PS_BF16_LAUNCH
     }
     const uint64_t nblocks = (uint64_t)N * PH * npwt;
