@@ -240,6 +240,13 @@ CONV_CASES = [
     dict(N=8, Cin=8, H=38, W=216, Cout=64, pool_k=4, pool_stride=4, scale=-0.7),  # 53
     dict(N=8, Cin=8, H=26, W=136, Cout=48, pool_k=3, pool_stride=3, conv_bias=False),
     dict(N=32, Cin=8, H=34, W=72, Cout=16, pool_k=2, pool_stride=2, scale=0.0),   # 35
+    # the same form with runs of several pooled rows per workgroup (64 images, so each
+    # plane splits into 8 runs): both ring phases and the row refill, for pool 2, 3, 4
+    # and 32 or 64 columns per strip
+    dict(N=64, Cin=8, H=50, W=72, Cout=16, pool_k=2, pool_stride=2),    # 3-row runs
+    dict(N=64, Cin=8, H=86, W=136, Cout=24, pool_k=3, pool_stride=3, scale=-0.9),
+    dict(N=64, Cin=8, H=82, W=128, Cout=32, pool_k=4, pool_stride=4),   # 31 columns
+    dict(N=64, Cin=7, H=65, W=96, Cout=40, pool_k=3, pool_stride=3),    # 31 columns
 ]
 
 
