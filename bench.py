@@ -72,18 +72,18 @@ TINY_FLOP = 2 * 72 * 2 * 16 * 28 * 28              # the 28x28 conv outputs the 
 # x1.0.  `src` is the hash of the kernel's sources when the counters were taken; a
 # kernel edited since then reports traffic null.  See profiles/traffic_*.md.
 TRAFFIC = {
-    "conv": {"src": "acd53f66d671af14", "fetch_bytes": 266692295, "write_bytes": 130649232},
-    "conv_bf16": {"src": "acd53f66d671af14", "fetch_bytes": 136587260, "write_bytes": 81220448},
-    "maxpool": {"src": "7fe7bbddd12793d9", "fetch_bytes": 2160265384, "write_bytes": 2140676736},
-    "maxpool_s2": {"src": "7fe7bbddd12793d9", "fetch_bytes": 2176862295, "write_bytes": 536870912},
-    "maxpool_d2": {"src": "7fe7bbddd12793d9", "fetch_bytes": 2266569258, "write_bytes": 2147483648},
-    "convT": {"src": "d41d08fdc4635d00", "fetch_bytes": 141249703, "write_bytes": 1256486288},
-    "convT_bf16": {"src": "712a7c1de94f1105", "fetch_bytes": 77606485, "write_bytes": 773801136},
-    "conv_general": {"src": "456ad05d0ed2d488", "fetch_bytes": 137132587, "write_bytes": 69301104},
-    "conv_2stage#0": {"src": "8cfb246101a56548", "fetch_bytes": 276390802, "write_bytes": 2116707312},
-    "conv_2stage#1": {"src": "8cfb246101a56548", "fetch_bytes": 2112061737, "write_bytes": 133770352},
-    "convT_2stage#0": {"src": "98a24a537c00e58f", "fetch_bytes": 141007151, "write_bytes": 1282438560},
-    "convT_2stage#1": {"src": "98a24a537c00e58f", "fetch_bytes": 1223700946, "write_bytes": 1121319552},
+    "conv": {"src": "024f76aa6b42ecd9", "fetch_bytes": 266662584, "write_bytes": 130644512},
+    "conv_bf16": {"src": "024f76aa6b42ecd9", "fetch_bytes": 136674033, "write_bytes": 80554352},
+    "maxpool": {"src": "7fe7bbddd12793d9", "fetch_bytes": 2160265127, "write_bytes": 2140757008},
+    "maxpool_s2": {"src": "7fe7bbddd12793d9", "fetch_bytes": 2176845077, "write_bytes": 536870912},
+    "maxpool_d2": {"src": "7fe7bbddd12793d9", "fetch_bytes": 2266539108, "write_bytes": 2147483648},
+    "convT": {"src": "d41d08fdc4635d00", "fetch_bytes": 141398490, "write_bytes": 1255964336},
+    "convT_bf16": {"src": "712a7c1de94f1105", "fetch_bytes": 77983492, "write_bytes": 773687376},
+    "conv_general": {"src": "456ad05d0ed2d488", "fetch_bytes": 137136226, "write_bytes": 69354144},
+    "conv_2stage#0": {"src": "8cfb246101a56548", "fetch_bytes": 277580507, "write_bytes": 2116681952},
+    "conv_2stage#1": {"src": "8cfb246101a56548", "fetch_bytes": 2112061547, "write_bytes": 133778864},
+    "convT_2stage#0": {"src": "98a24a537c00e58f", "fetch_bytes": 140880299, "write_bytes": 1281346448},
+    "convT_2stage#1": {"src": "98a24a537c00e58f", "fetch_bytes": 1223701577, "write_bytes": 1121259120},
 }
 KERNEL_SOURCES = {
     "conv": ["conv_pool.hip", "ps_internal.h"],
