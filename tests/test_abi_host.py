@@ -53,6 +53,18 @@ def test_header_symbols_are_exported(ps):
         assert hasattr(lib, s), s
 
 
+def test_no_undefined_kernel_handles(ps):
+    """Every kernel the library launches is defined in it: the host pass of the compiler
+    can drop a kernel's launch handle without a diagnostic, which would otherwise show
+    only when the library is loaded on a device."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "ps_build", os.path.join(ROOT, "pool_stencil_amd", "build.py"))
+    build = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(build)
+    assert build._undefined_own_symbols(ps.LIB_PATH) == []
+
+
 def test_status_strings(ps):
     for st in range(7):
         s = ps.status_string(st)
