@@ -72,18 +72,18 @@ TINY_FLOP = 2 * 72 * 2 * 16 * 28 * 28              # the 28x28 conv outputs the 
 # x1.0.  `src` is the hash of the kernel's sources when the counters were taken; a
 # kernel edited since then reports traffic null.  See profiles/traffic_*.md.
 TRAFFIC = {
-    "conv": {"src": "024f76aa6b42ecd9", "fetch_bytes": 266662584, "write_bytes": 130644512},
-    "conv_bf16": {"src": "024f76aa6b42ecd9", "fetch_bytes": 136674033, "write_bytes": 80554352},
-    "maxpool": {"src": "7fe7bbddd12793d9", "fetch_bytes": 2160265127, "write_bytes": 2140757008},
-    "maxpool_s2": {"src": "7fe7bbddd12793d9", "fetch_bytes": 2176845077, "write_bytes": 536870912},
-    "maxpool_d2": {"src": "7fe7bbddd12793d9", "fetch_bytes": 2266539108, "write_bytes": 2147483648},
-    "convT": {"src": "d41d08fdc4635d00", "fetch_bytes": 141398490, "write_bytes": 1255964336},
-    "convT_bf16": {"src": "712a7c1de94f1105", "fetch_bytes": 77983492, "write_bytes": 773687376},
-    "conv_general": {"src": "456ad05d0ed2d488", "fetch_bytes": 137136226, "write_bytes": 69354144},
-    "conv_2stage#0": {"src": "8cfb246101a56548", "fetch_bytes": 277580507, "write_bytes": 2116681952},
-    "conv_2stage#1": {"src": "8cfb246101a56548", "fetch_bytes": 2112061547, "write_bytes": 133778864},
-    "convT_2stage#0": {"src": "98a24a537c00e58f", "fetch_bytes": 140880299, "write_bytes": 1281346448},
-    "convT_2stage#1": {"src": "98a24a537c00e58f", "fetch_bytes": 1223701577, "write_bytes": 1121259120},
+    "conv": {"src": "024f76aa6b42ecd9", "fetch_bytes": 266662632, "write_bytes": 130655952},
+    "conv_bf16": {"src": "024f76aa6b42ecd9", "fetch_bytes": 136674057, "write_bytes": 81105072},
+    "maxpool": {"src": "7fe7bbddd12793d9", "fetch_bytes": 2160265577, "write_bytes": 2140728224},
+    "maxpool_s2": {"src": "7fe7bbddd12793d9", "fetch_bytes": 2176849115, "write_bytes": 536870912},
+    "maxpool_d2": {"src": "7fe7bbddd12793d9", "fetch_bytes": 2266397054, "write_bytes": 2147483648},
+    "convT": {"src": "4f59338f0b6ec306", "fetch_bytes": 141412979, "write_bytes": 1257060128},
+    "convT_bf16": {"src": "ddd808cd9ea2198b", "fetch_bytes": 78853622, "write_bytes": 775141568},
+    "conv_general": {"src": "456ad05d0ed2d488", "fetch_bytes": 137116219, "write_bytes": 69326320},
+    "conv_2stage#0": {"src": "8cfb246101a56548", "fetch_bytes": 277680650, "write_bytes": 2116858896},
+    "conv_2stage#1": {"src": "8cfb246101a56548", "fetch_bytes": 2112062053, "write_bytes": 133775056},
+    "convT_2stage#0": {"src": "ee271e1a43173546", "fetch_bytes": 140852869, "write_bytes": 1283158112},
+    "convT_2stage#1": {"src": "ee271e1a43173546", "fetch_bytes": 1223781537, "write_bytes": 1121302384},
 }
 KERNEL_SOURCES = {
     "conv": ["conv_pool.hip", "ps_internal.h"],
