@@ -42,6 +42,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace ps {
 namespace {
 
@@ -313,28 +315,38 @@ __global__ __launch_bounds__(kThreads) void convT_rows_f32(
         // while group k's 32 MFMAs run; inside a group the 8 accumulators alternate, so
         // an MFMA never waits on the one before it.  Scheduling barriers keep that order
         // (left alone, the compiler waited on each read right before its first use and
-        // chained dependent MFMAs).
-        f32x4 bv[2][4];
+        // chained dependent MFMAs).  NBK: position blocks computed (a plane's last tile
+        // with at most 16 positions computes one; the other blocks keep the bias and
+        // their outputs are dropped).
+        auto kloop = [&](auto nbk_c) {
+            constexpr int NBK = decltype(nbk_c)::value;
+            f32x4 bv[2][4];
 #pragma unroll
-        for (int bk = 0; bk < 4; ++bk) bv[0][bk] = read_b(bk, 0);
+            for (int bk = 0; bk < NBK; ++bk) bv[0][bk] = read_b(bk, 0);
 #pragma unroll
-        for (int k = 0; k < 4 * CQ; ++k) {
-            const int q = k >> 2, tp = k & 3;
-            if (k + 1 < 4 * CQ) {
+            for (int k = 0; k < 4 * CQ; ++k) {
+                const int q = k >> 2, tp = k & 3;
+                if (k + 1 < 4 * CQ) {
 #pragma unroll
-                for (int bk = 0; bk < 4; ++bk) bv[(k + 1) & 1][bk] = read_b(bk, k + 1);
+                    for (int bk = 0; bk < NBK; ++bk) bv[(k + 1) & 1][bk] = read_b(bk, k + 1);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+#pragma unroll
+                    for (int bk = 0; bk < NBK; ++bk)
+#pragma unroll
+                        for (int b = 0; b < 2; ++b)
+                            acc[b][bk] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                                wr[b][q][tp][s], bv[k & 1][bk][s], acc[b][bk], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
             }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-#pragma unroll
-                for (int bk = 0; bk < 4; ++bk)
-#pragma unroll
-                    for (int b = 0; b < 2; ++b)
-                        acc[b][bk] = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                            wr[b][q][tp][s], bv[k & 1][bk][s], acc[b][bk], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
-        }
+        };
+        // (the class-0 plane of the workload, 65 x 65 positions, ends in a tile of one)
+        if (T == ntile - 1 && plane_pos - T * kTP <= 16)
+            kloop(std::integral_constant<int, 1>{});
+        else
+            kloop(std::integral_constant<int, 4>{});
 
         // the new row goes to a slot that tile T does not read
         fill_store(nhi, has_new, pv);
