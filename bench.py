@@ -72,18 +72,18 @@ TINY_FLOP = 2 * 72 * 2 * 16 * 28 * 28              # the 28x28 conv outputs the 
 # x1.0.  `src` is the hash of the kernel's sources when the counters were taken; a
 # kernel edited since then reports traffic null.  See profiles/traffic_*.md.
 TRAFFIC = {
-    "conv": {"src": "024f76aa6b42ecd9", "fetch_bytes": 266662632, "write_bytes": 130655952},
-    "conv_bf16": {"src": "024f76aa6b42ecd9", "fetch_bytes": 136674057, "write_bytes": 81105072},
-    "maxpool": {"src": "7fe7bbddd12793d9", "fetch_bytes": 2160265577, "write_bytes": 2140728224},
-    "maxpool_s2": {"src": "7fe7bbddd12793d9", "fetch_bytes": 2176849115, "write_bytes": 536870912},
-    "maxpool_d2": {"src": "7fe7bbddd12793d9", "fetch_bytes": 2266397054, "write_bytes": 2147483648},
-    "convT": {"src": "4f59338f0b6ec306", "fetch_bytes": 141412979, "write_bytes": 1257060128},
-    "convT_bf16": {"src": "ddd808cd9ea2198b", "fetch_bytes": 78853622, "write_bytes": 775141568},
-    "conv_general": {"src": "456ad05d0ed2d488", "fetch_bytes": 137116219, "write_bytes": 69326320},
-    "conv_2stage#0": {"src": "8cfb246101a56548", "fetch_bytes": 277680650, "write_bytes": 2116858896},
-    "conv_2stage#1": {"src": "8cfb246101a56548", "fetch_bytes": 2112062053, "write_bytes": 133775056},
-    "convT_2stage#0": {"src": "ee271e1a43173546", "fetch_bytes": 140852869, "write_bytes": 1283158112},
-    "convT_2stage#1": {"src": "ee271e1a43173546", "fetch_bytes": 1223781537, "write_bytes": 1121302384},
+    "conv": {"src": "024f76aa6b42ecd9", "fetch_bytes": 266662568, "write_bytes": 130646656},
+    "conv_bf16": {"src": "024f76aa6b42ecd9", "fetch_bytes": 136674025, "write_bytes": 80061744},
+    "maxpool": {"src": "7fe7bbddd12793d9", "fetch_bytes": 2160264806, "write_bytes": 2140710736},
+    "maxpool_s2": {"src": "7fe7bbddd12793d9", "fetch_bytes": 2176852435, "write_bytes": 536870912},
+    "maxpool_d2": {"src": "7fe7bbddd12793d9", "fetch_bytes": 2266660825, "write_bytes": 2147483648},
+    "convT": {"src": "6bcf64774038c99d", "fetch_bytes": 142739559, "write_bytes": 1257164144},
+    "convT_bf16": {"src": "795616b272b40138", "fetch_bytes": 78763430, "write_bytes": 773598880},
+    "conv_general": {"src": "456ad05d0ed2d488", "fetch_bytes": 137129498, "write_bytes": 69352656},
+    "conv_2stage#0": {"src": "8cfb246101a56548", "fetch_bytes": 276823971, "write_bytes": 2116772048},
+    "conv_2stage#1": {"src": "8cfb246101a56548", "fetch_bytes": 2112061421, "write_bytes": 133778672},
+    "convT_2stage#0": {"src": "47c330d902d0d16e", "fetch_bytes": 141292053, "write_bytes": 1352989936},
+    "convT_2stage#1": {"src": "47c330d902d0d16e", "fetch_bytes": 1223667009, "write_bytes": 1121198160},
 }
 KERNEL_SOURCES = {
     "conv": ["conv_pool.hip", "ps_internal.h"],
