@@ -350,6 +350,10 @@ CONVT_ROWS_CASES = [
     dict(N=1, Cin=16, H=9, W=84, Cout=128),
     dict(N=1, Cin=8, H=6, W=68, Cout=128, pad=5),
     dict(N=64, Cin=64, H=6, W=64, Cout=128),
+    # a plane's last tile of at most 16 positions runs one position block's matrix work:
+    # last tiles of 16 and 15 positions (one block), then 17 and 16
+    dict(N=1, Cin=32, H=15, W=64, Cout=128),
+    dict(N=1, Cin=32, H=16, W=64, Cout=128, scale=-0.9),
 ]
 CONVT_CASES += CONVT_ROWS_CASES
 
